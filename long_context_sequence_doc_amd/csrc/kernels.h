@@ -1,0 +1,60 @@
+// Kernel launchers (internal). Each returns hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "sap_internal.h"
+
+namespace sap {
+
+struct FwdLaunch {
+  const void *q, *k, *v;
+  int64_t q_row_stride, kv_row_stride;
+  int32_t hq, hkv, d;
+  float scale;
+  float *o, *lse;
+  int32_t tq;
+  const WorkItem *work;
+  const WorkRange *range;
+  const PartnerEntry *partners;
+  const int32_t *ds_q;
+  int32_t n_work;
+};
+
+hipError_t launch_attn_fwd(const FwdLaunch &a, hipStream_t stream);
+
+struct MergeLaunch {
+  float *o_acc, *lse_acc;
+  const float *o_part, *lse_part;
+  int32_t tq, hq, d;
+  const int32_t *touched_rows;  // device (local_start, n) pairs; nullptr = all rows
+  int32_t n_touched;
+  int32_t max_rows;             // rows of the largest touched tile
+};
+
+hipError_t launch_lse_merge(const MergeLaunch &a, hipStream_t stream);
+
+struct BwdLaunch {
+  const void *q, *k, *v, *dout;
+  const float *o, *lse;
+  int64_t q_row_stride, kv_row_stride;
+  int32_t hq, hkv, d;
+  float scale;
+  float *dq, *dk, *dv;
+  float *delta;                 // workspace [hq][tq]
+  int32_t tq;
+  const int32_t *touched_rows;  // Q tiles of the plan: (local_start, n) pairs
+  int32_t n_touched_q;
+  int32_t max_q_rows;
+  const WorkItem *work;         // KV-major work
+  const WorkRange *range;
+  const PartnerEntry *partners;
+  const int32_t *ds_q;
+  int32_t n_work;
+};
+
+hipError_t launch_attn_bwd(const BwdLaunch &a, hipStream_t stream);
+
+}  // namespace sap

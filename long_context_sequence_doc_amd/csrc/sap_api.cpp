@@ -1,0 +1,296 @@
+// C ABI of libsap: argument checks, plan lifetime and kernel dispatch.
+// Every check runs on the host before anything is launched; no C++
+// exception crosses the ABI.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "kernels.h"
+#include "sap_internal.h"
+
+struct sap_plan_s {
+  sap::Plan p;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sap_status fail(sap_status s, const std::string &msg) {
+  g_last_error = msg;
+  return s;
+}
+
+sap_status ok() {
+  g_last_error.clear();
+  return SAP_OK;
+}
+
+sap_status hip_fail(hipError_t e, const char *what) {
+  return fail(SAP_ERR_HIP, std::string(what) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")");
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+template <class T>
+size_t bytes_of(const std::vector<T> &v) { return v.size() * sizeof(T); }
+
+sap_status check_heads(int32_t hq, int32_t hkv, int32_t d) {
+  if (hq <= 0 || hkv <= 0 || hq % hkv != 0) return fail(SAP_ERR_INVALID_ARG, "need hq > 0, hkv > 0, hq % hkv == 0");
+  if (d != 64 && d != 128) return fail(SAP_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  return SAP_OK;
+}
+
+// A plan with work must be uploaded to the current device before a launch.
+sap_status check_uploaded(sap_plan_t plan) {
+  if (!plan->p.dev.base) return fail(SAP_ERR_STATE, "plan has not been uploaded (call sap_plan_upload)");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != plan->p.dev.device)
+    return fail(SAP_ERR_STATE, "plan was uploaded to another device");
+  return SAP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sap_version(void) { return 100; }
+
+const char *sap_last_error(void) { return g_last_error.c_str(); }
+
+sap_status sap_plan(const int32_t *cu_seqlens, int32_t n_docs, const sap_segment *q_segs,
+                    int32_t n_q_segs, const sap_segment *kv_segs, int32_t n_kv_segs,
+                    int32_t block_m, int32_t block_n, sap_plan_t *out) {
+  if (!out) return fail(SAP_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  sap_plan_s *h = new (std::nothrow) sap_plan_s();
+  if (!h) return fail(SAP_ERR_NO_MEMORY, "plan allocation failed");
+  std::string err;
+  sap_status s;
+  try {
+    s = sap::build_plan(cu_seqlens, n_docs, q_segs, n_q_segs, kv_segs, n_kv_segs, block_m, block_n, &h->p, &err);
+  } catch (const std::bad_alloc &) {
+    s = SAP_ERR_NO_MEMORY;
+    err = "host memory exhausted while planning";
+  } catch (...) {
+    s = SAP_ERR_INVALID_ARG;
+    err = "planner failed";
+  }
+  if (s != SAP_OK) {
+    delete h;
+    return fail(s, err);
+  }
+  *out = h;
+  return ok();
+}
+
+sap_status sap_plan_upload(sap_plan_t plan, void *hip_stream) {
+  if (!plan) return fail(SAP_ERR_INVALID_ARG, "plan is NULL");
+  sap::Plan &P = plan->p;
+  if (P.dev.base) return ok();
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  // one allocation; each table 256-byte aligned
+  size_t off[8], total = 0;
+  const void *src[8] = {P.q_work.data(), P.q_range.data(), P.q_partners.data(), P.kv_work.data(),
+                        P.kv_range.data(), P.kv_partners.data(), P.ds_q.data(), P.touched_rows.data()};
+  size_t len[8] = {bytes_of(P.q_work), bytes_of(P.q_range), bytes_of(P.q_partners), bytes_of(P.kv_work),
+                   bytes_of(P.kv_range), bytes_of(P.kv_partners), bytes_of(P.ds_q), bytes_of(P.touched_rows)};
+  for (int i = 0; i < 8; ++i) {
+    off[i] = total;
+    total += align_up(std::max<size_t>(len[i], 1));
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  void *base = nullptr;
+  e = hipMalloc(&base, total);
+  if (e == hipErrorOutOfMemory) return fail(SAP_ERR_NO_MEMORY, "hipMalloc of plan tables failed");
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc");
+  for (int i = 0; i < 8; ++i) {
+    if (!len[i]) continue;
+    e = hipMemcpyAsync(static_cast<char *>(base) + off[i], src[i], len[i], hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) {
+      (void)hipFree(base);
+      return hip_fail(e, "hipMemcpyAsync of plan tables");
+    }
+  }
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) {
+    (void)hipFree(base);
+    return hip_fail(e, "hipStreamSynchronize after plan upload");
+  }
+  char *b = static_cast<char *>(base);
+  P.dev.base = base;
+  P.dev.bytes = total;
+  P.dev.q_work = reinterpret_cast<const sap::WorkItem *>(b + off[0]);
+  P.dev.q_range = reinterpret_cast<const sap::WorkRange *>(b + off[1]);
+  P.dev.q_partners = reinterpret_cast<const sap::PartnerEntry *>(b + off[2]);
+  P.dev.kv_work = reinterpret_cast<const sap::WorkItem *>(b + off[3]);
+  P.dev.kv_range = reinterpret_cast<const sap::WorkRange *>(b + off[4]);
+  P.dev.kv_partners = reinterpret_cast<const sap::PartnerEntry *>(b + off[5]);
+  P.dev.ds_q = reinterpret_cast<const int32_t *>(b + off[6]);
+  P.dev.touched_rows = reinterpret_cast<const int32_t *>(b + off[7]);
+  P.dev.device = dev;
+  return ok();
+}
+
+sap_status sap_plan_info(sap_plan_t plan, sap_plan_stats *out) {
+  if (!plan || !out) return fail(SAP_ERR_INVALID_ARG, "plan or out is NULL");
+  const sap::Plan &P = plan->p;
+  std::memset(out, 0, sizeof(*out));
+  out->n_tiles = int64_t(P.q_tile.size());
+  out->n_full = P.n_class[SAP_TILE_FULL];
+  out->n_diagonal = P.n_class[SAP_TILE_DIAGONAL];
+  out->n_partial = P.n_class[SAP_TILE_PARTIAL];
+  out->useful_pairs_per_head = P.useful;
+  out->n_q_tiles = int32_t(P.q_tiles.size());
+  out->n_kv_tiles = int32_t(P.kv_tiles.size());
+  out->n_touched_q_tiles = int32_t(P.touched.size());
+  out->n_touched_kv_tiles = P.n_touched_kv;
+  out->tq = P.tq;
+  out->tkv = P.tkv;
+  out->block_m = P.bm;
+  out->block_n = P.bn;
+  out->uploaded = P.dev.base ? 1 : 0;
+  return ok();
+}
+
+sap_status sap_plan_tiles(sap_plan_t plan, int32_t *q_tile, int32_t *kv_tile, uint8_t *cls, int64_t cap) {
+  if (!plan) return fail(SAP_ERR_INVALID_ARG, "plan is NULL");
+  const sap::Plan &P = plan->p;
+  const int64_t n = int64_t(P.q_tile.size());
+  if (cap < n) return fail(SAP_ERR_INVALID_ARG, "capacity smaller than n_tiles");
+  if (n == 0) return ok();
+  if (q_tile) std::memcpy(q_tile, P.q_tile.data(), size_t(n) * 4);
+  if (kv_tile) std::memcpy(kv_tile, P.kv_tile.data(), size_t(n) * 4);
+  if (cls) std::memcpy(cls, P.cls.data(), size_t(n));
+  return ok();
+}
+
+sap_status sap_plan_q_tiles(sap_plan_t plan, int32_t *touched, int32_t cap_touched, int32_t *desc,
+                            int32_t cap_desc) {
+  if (!plan) return fail(SAP_ERR_INVALID_ARG, "plan is NULL");
+  const sap::Plan &P = plan->p;
+  if (touched) {
+    if (cap_touched < int32_t(P.touched.size())) return fail(SAP_ERR_INVALID_ARG, "touched capacity too small");
+    std::copy(P.touched.begin(), P.touched.end(), touched);
+  }
+  if (desc) {
+    if (cap_desc < 3 * int32_t(P.q_tiles.size())) return fail(SAP_ERR_INVALID_ARG, "desc capacity too small");
+    for (size_t i = 0; i < P.q_tiles.size(); ++i) {
+      desc[3 * i] = P.q_tiles[i].local_start;
+      desc[3 * i + 1] = P.q_tiles[i].n;
+      desc[3 * i + 2] = P.q_tiles[i].global_start;
+    }
+  }
+  return ok();
+}
+
+void sap_plan_free(sap_plan_t plan) {
+  if (!plan) return;
+  if (plan->p.dev.base) (void)hipFree(plan->p.dev.base);
+  delete plan;
+}
+
+sap_status sap_attn_fwd(sap_plan_t plan, const void *q, const void *k, const void *v,
+                        int64_t q_row_stride, int64_t kv_row_stride, int32_t hq, int32_t hkv,
+                        int32_t d, float scale, float *o, float *lse, void *hip_stream) {
+  if (!plan) return fail(SAP_ERR_INVALID_ARG, "plan is NULL");
+  sap_status s = check_heads(hq, hkv, d);
+  if (s != SAP_OK) return s;
+  const sap::Plan &P = plan->p;
+  if (P.bm != 128 || P.bn != 64) return fail(SAP_ERR_UNSUPPORTED, "forward needs a 128 x 64 plan");
+  if (!(scale > 0.f) || !(scale < 1e30f)) return fail(SAP_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (P.q_work.empty()) return ok();
+  if ((s = check_uploaded(plan)) != SAP_OK) return s;
+  if (!q || !k || !v || !o || !lse) return fail(SAP_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return fail(SAP_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (q_row_stride < int64_t(hq) * d || q_row_stride % 8) return fail(SAP_ERR_INVALID_ARG, "q_row_stride must be >= hq*d and a multiple of 8");
+  if (kv_row_stride < int64_t(hkv) * d || kv_row_stride % 8) return fail(SAP_ERR_INVALID_ARG, "kv_row_stride must be >= hkv*d and a multiple of 8");
+  sap::FwdLaunch a{};
+  a.q = q; a.k = k; a.v = v;
+  a.q_row_stride = q_row_stride; a.kv_row_stride = kv_row_stride;
+  a.hq = hq; a.hkv = hkv; a.d = d; a.scale = scale;
+  a.o = o; a.lse = lse; a.tq = P.tq;
+  a.work = P.dev.q_work; a.range = P.dev.q_range; a.partners = P.dev.q_partners; a.ds_q = P.dev.ds_q;
+  a.n_work = int32_t(P.q_work.size());
+  hipError_t e = sap::launch_attn_fwd(a, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
+  return ok();
+}
+
+sap_status sap_lse_merge(sap_plan_t plan, float *o_acc, float *lse_acc, const float *o_part,
+                         const float *lse_part, int32_t tq, int32_t hq, int32_t d, void *hip_stream) {
+  if (hq <= 0 || d < 4 || d > 256 || (d & (d - 1))) return fail(SAP_ERR_INVALID_ARG, "need hq > 0 and d a power of two in [4, 256]");
+  if (tq < 0) return fail(SAP_ERR_INVALID_ARG, "tq < 0");
+  sap::MergeLaunch a{};
+  if (plan) {
+    if (tq != plan->p.tq) return fail(SAP_ERR_INVALID_ARG, "tq differs from the plan's local Q rows");
+    if (plan->p.touched.empty()) return ok();
+    sap_status s = check_uploaded(plan);
+    if (s != SAP_OK) return s;
+    a.touched_rows = plan->p.dev.touched_rows;
+    a.n_touched = int32_t(plan->p.touched.size());
+    a.max_rows = plan->p.bm;
+  } else {
+    a.touched_rows = nullptr;
+    a.n_touched = tq > 0 ? 1 : 0;
+    a.max_rows = tq;
+  }
+  if (a.n_touched == 0) return ok();
+  if (!o_acc || !lse_acc || !o_part || !lse_part) return fail(SAP_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(o_acc) || !aligned16(o_part)) return fail(SAP_ERR_INVALID_ARG, "O pointers must be 16-byte aligned");
+  a.o_acc = o_acc; a.lse_acc = lse_acc; a.o_part = o_part; a.lse_part = lse_part;
+  a.tq = tq; a.hq = hq; a.d = d;
+  hipError_t e = sap::launch_lse_merge(a, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "lse_merge launch");
+  return ok();
+}
+
+size_t sap_attn_bwd_workspace(sap_plan_t plan, int32_t hq, int32_t d) {
+  (void)d;
+  if (!plan || hq <= 0) return 0;
+  return align_up(size_t(hq) * size_t(std::max(plan->p.tq, 1)) * sizeof(float));
+}
+
+sap_status sap_attn_bwd(sap_plan_t plan, const void *q, const void *k, const void *v, const float *o,
+                        const float *lse_final, const void *dout, int64_t q_row_stride,
+                        int64_t kv_row_stride, int32_t hq, int32_t hkv, int32_t d, float scale,
+                        float *dq, float *dk, float *dv, void *workspace, size_t workspace_bytes,
+                        void *hip_stream) {
+  if (!plan) return fail(SAP_ERR_INVALID_ARG, "plan is NULL");
+  sap_status s = check_heads(hq, hkv, d);
+  if (s != SAP_OK) return s;
+  const sap::Plan &P = plan->p;
+  if (P.bm != 64 || P.bn != 128) return fail(SAP_ERR_UNSUPPORTED, "backward needs a 64 x 128 plan");
+  if (!(scale > 0.f) || !(scale < 1e30f)) return fail(SAP_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (P.kv_work.empty()) return ok();
+  if ((s = check_uploaded(plan)) != SAP_OK) return s;
+  if (!q || !k || !v || !o || !lse_final || !dout || !dq || !dk || !dv || !workspace)
+    return fail(SAP_ERR_INVALID_ARG, "NULL pointer");
+  const void *ptrs[] = {q, k, v, o, lse_final, dout, dq, dk, dv, workspace};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return fail(SAP_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (workspace_bytes < sap_attn_bwd_workspace(plan, hq, d)) return fail(SAP_ERR_INVALID_ARG, "workspace too small");
+  if (q_row_stride < int64_t(hq) * d || q_row_stride % 8) return fail(SAP_ERR_INVALID_ARG, "q_row_stride must be >= hq*d and a multiple of 8");
+  if (kv_row_stride < int64_t(hkv) * d || kv_row_stride % 8) return fail(SAP_ERR_INVALID_ARG, "kv_row_stride must be >= hkv*d and a multiple of 8");
+  sap::BwdLaunch a{};
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.o = o; a.lse = lse_final;
+  a.q_row_stride = q_row_stride; a.kv_row_stride = kv_row_stride;
+  a.hq = hq; a.hkv = hkv; a.d = d; a.scale = scale;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.delta = static_cast<float *>(workspace); a.tq = P.tq;
+  a.touched_rows = P.dev.touched_rows; a.n_touched_q = int32_t(P.touched.size()); a.max_q_rows = P.bm;
+  a.work = P.dev.kv_work; a.range = P.dev.kv_range; a.partners = P.dev.kv_partners; a.ds_q = P.dev.ds_q;
+  a.n_work = int32_t(P.kv_work.size());
+  hipError_t e = sap::launch_attn_bwd(a, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "attn_bwd launch");
+  return ok();
+}
+
+}  // extern "C"

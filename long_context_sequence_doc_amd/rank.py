@@ -1,0 +1,91 @@
+"""One sequence-parallel rank's forward: its ring steps issued through the C ABI.
+
+The SP blog page (bmjup.com/post/14448.html, core principles) describes the
+ring: each GPU holds one token chunk of Q and the KV chunks pass round the
+ring, so after P steps every rank holds the full-sequence result for its
+rows. Here the KV chunks of every step are already resident (they are views
+into whole-sequence K/V buffers, selected by each step's segment table), and
+one rank's work is:
+
+    step 0 (the rank's own chunks; every local row sees at least itself):
+        sap_attn_fwd -> running O / LSE
+    each later step whose plan lists any tile:
+        sap_attn_fwd -> partial O / LSE of the touched rows
+        sap_lse_merge   (touched rows only; the others are exact as they are)
+    steps with no tile launch nothing -- the sequence-aware part: with
+    document masks most remote chunks of a rank hold no key its rows may see.
+
+A head-sharded (Ulysses) rank is the one-step case with Q = KV = the whole
+sequence for its heads.
+"""
+from __future__ import annotations
+
+from typing import List, Sequence, Tuple
+
+import torch
+
+from . import (sap_attn_fwd, sap_lse_merge, sap_plan, sap_plan_free, sap_plan_info, sap_plan_q_tiles,
+               sap_plan_upload)
+
+BLOCK_M, BLOCK_N = 128, 64
+
+
+class RankForward:
+    def __init__(self, cu_seqlens, q_segs: Sequence[Tuple[int, int, int]],
+                 step_kv_segs: List[Sequence[Tuple[int, int, int]]], hq: int, hkv: int, d: int,
+                 scale: float, device: str = "cuda"):
+        self.hq, self.hkv, self.d, self.scale = hq, hkv, d, scale
+        self.plans = [sap_plan(cu_seqlens, q_segs, kv, BLOCK_M, BLOCK_N) for kv in step_kv_segs]
+        self.infos = [sap_plan_info(p) for p in self.plans]
+        first = self.infos[0]
+        if first["n_touched_q_tiles"] != first["n_q_tiles"]:
+            raise ValueError("step 0 must hold the rank's own chunks (it has to touch every local Q tile)")
+        self.tq = first["tq"]
+        self.active = [i for i, inf in enumerate(self.infos) if inf["n_tiles"] > 0]
+        for i in self.active:
+            sap_plan_upload(self.plans[i])
+        self.o = torch.empty((self.tq, hq, d), dtype=torch.float32, device=device)
+        self.lse = torch.empty((hq, self.tq), dtype=torch.float32, device=device)
+        need_part = len(self.active) > 1
+        self.o_part = torch.empty_like(self.o) if need_part else None
+        self.lse_part = torch.empty_like(self.lse) if need_part else None
+
+    @property
+    def useful_pairs_per_head(self) -> int:
+        return sum(inf["useful_pairs_per_head"] for inf in self.infos)
+
+    @property
+    def useful_flop(self) -> float:
+        """Forward FLOP counted on allowed (query, key) pairs only: 4 D per pair per query head."""
+        return 4.0 * self.d * self.hq * self.useful_pairs_per_head
+
+    def merge_rows(self) -> int:
+        """(row, head) pairs merged per run (touched rows of every step after the first)."""
+        rows = 0
+        for i in self.active[1:]:
+            touched, desc = sap_plan_q_tiles(self.plans[i])
+            rows += int(desc[touched, 1].sum())
+        return rows * self.hq
+
+    def touched_rows(self, step: int):
+        """Local Q rows the given step's forward writes."""
+        touched, desc = sap_plan_q_tiles(self.plans[step])
+        return [r for t in touched for r in range(desc[t, 0], desc[t, 0] + desc[t, 1])]
+
+    def run(self, q, k, v, q_row_stride: int, kv_row_stride: int, stream=None):
+        """q: local Q rows [tq, hq, d] bf16; k, v: buffers addressed by the steps' local rows."""
+        for n, i in enumerate(self.active):
+            p = self.plans[i]
+            if n == 0:
+                sap_attn_fwd(p, q, k, v, q_row_stride, kv_row_stride, self.hq, self.hkv, self.d, self.scale,
+                             self.o, self.lse, stream)
+            else:
+                sap_attn_fwd(p, q, k, v, q_row_stride, kv_row_stride, self.hq, self.hkv, self.d, self.scale,
+                             self.o_part, self.lse_part, stream)
+                sap_lse_merge(p, self.o, self.lse, self.o_part, self.lse_part, self.tq, self.hq, self.d, stream)
+        return self.o, self.lse
+
+    def close(self):
+        for p in self.plans:
+            sap_plan_free(p)
+        self.plans = []

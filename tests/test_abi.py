@@ -1,0 +1,92 @@
+"""The C ABI library on the host: it loads, exports every declared symbol, and
+rejects bad arguments before anything reaches the GPU (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import long_context_sequence_doc_amd as sap
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "sap.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sap_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    names = _declared()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(sap.lib_path)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in sap.EXPORTED, n
+    assert sap.sap_version() >= 100
+
+
+def _plan(cu=(0, 100), q=((0, 100, 0),), kv=((0, 100, 0),), bm=128, bn=64):
+    return sap.sap_plan(list(cu), list(q), list(kv), bm, bn)
+
+
+@pytest.mark.parametrize("cu,q,kv,bm,bn,msg", [
+    ((5, 100), ((0, 10, 0),), (), 128, 64, "cu_seqlens[0]"),
+    ((0, 50, 40), ((0, 10, 0),), (), 128, 64, "non-decreasing"),
+    ((0, 100), ((0, 101, 0),), (), 128, 64, "out of range"),
+    ((0, 100), ((0, 50, 0), (40, 60, 50)), (), 128, 64, "global ranges overlap"),
+    ((0, 100), ((0, 50, 0), (60, 80, 10)), (), 128, 64, "local row ranges overlap"),
+    ((0, 100), ((0, 50, 0),), ((0, 10, 0), (5, 20, 10)), 128, 64, "global ranges overlap"),
+    ((0, 100), ((0, 50, 0),), (), 96, 64, "block_m"),
+    ((0, 100), ((10, 5, 0),), (), 128, 64, "out of range"),
+])
+def test_plan_rejects_bad_arguments(cu, q, kv, bm, bn, msg):
+    with pytest.raises(sap.SapError) as e:
+        sap.sap_plan(list(cu), list(q), list(kv), bm, bn)
+    assert e.value.status == sap.SAP_ERR_INVALID_ARG
+    assert msg in str(e.value)
+
+
+def test_compute_calls_validate_before_launch():
+    p = _plan()
+    # unsupported head_dim / bad heads / wrong tile shape / not uploaded: nothing is launched
+    with pytest.raises(sap.SapError) as e:
+        sap.sap_attn_fwd(p, 16, 16, 16, 96, 96, 1, 1, 96, 0.1, 16, 16, stream=0)
+    assert e.value.status == sap.SAP_ERR_UNSUPPORTED
+    with pytest.raises(sap.SapError) as e:
+        sap.sap_attn_fwd(p, 16, 16, 16, 128, 128, 3, 2, 64, 0.1, 16, 16, stream=0)
+    assert e.value.status == sap.SAP_ERR_INVALID_ARG
+    with pytest.raises(sap.SapError) as e:
+        sap.sap_attn_fwd(p, 16, 16, 16, 128, 128, 2, 2, 64, 0.1, 16, 16, stream=0)
+    assert e.value.status == sap.SAP_ERR_STATE
+    with pytest.raises(sap.SapError) as e:
+        sap.sap_attn_fwd(p, 16, 16, 16, 128, 128, 2, 2, 64, -1.0, 16, 16, stream=0)
+    assert e.value.status == sap.SAP_ERR_INVALID_ARG
+    pb = _plan(bm=128, bn=64)
+    with pytest.raises(sap.SapError) as e:
+        sap.sap_attn_bwd(pb, 16, 16, 16, 16, 16, 16, 128, 128, 2, 2, 64, 0.1, 16, 16, 16, 16, 1 << 20, stream=0)
+    assert e.value.status == sap.SAP_ERR_UNSUPPORTED
+    with pytest.raises(sap.SapError) as e:
+        sap.sap_lse_merge(p, 16, 16, 16, 16, 99, 2, 64, stream=0)
+    assert e.value.status == sap.SAP_ERR_INVALID_ARG and "tq" in str(e.value)
+    with pytest.raises(sap.SapError) as e:
+        sap.sap_lse_merge(None, 16, 16, 16, 16, 100, 2, 96, stream=0)
+    assert e.value.status == sap.SAP_ERR_INVALID_ARG
+    with pytest.raises(sap.SapError):
+        sap.sap_lse_merge(None, 0, 16, 16, 16, 100, 2, 64, stream=0)
+
+
+def test_empty_calls_launch_nothing():
+    # a KV step that touches no Q tile: every compute call returns at once
+    p = sap.sap_plan([0, 100, 200], [(100, 200, 0)], [(0, 100, 0)], 128, 64)
+    info = sap.sap_plan_info(p)
+    assert info["n_tiles"] == 0 and info["n_touched_q_tiles"] == 0
+    sap.sap_attn_fwd(p, 0, 0, 0, 128, 128, 2, 2, 64, 0.125, 0, 0, stream=0)
+    sap.sap_lse_merge(p, 0, 0, 0, 0, 100, 2, 64, stream=0)
+
+
+def test_workspace_size():
+    p = _plan(bm=64, bn=128)
+    assert sap.sap_attn_bwd_workspace(p, 5, 128) >= 5 * 100 * 4

@@ -1,0 +1,248 @@
+"""GPU parity of the forward kernel and the merge against the fp64 oracle.
+
+Every call goes through the C ABI (libsap.so). Tolerances: max-abs 2e-2 on
+O, 1e-3 on finite LSE, -inf LSE matched exactly; the kernels see bf16 inputs
+and the oracle the same values widened to fp64.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention as A
+from tests.gpu_common import TOL_O, compare, f64, need_gpu, sample_rows, say, tensors, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _sap():
+    need_gpu()
+    import long_context_sequence_doc_amd as sap
+    return sap
+
+
+def _run_single(sap, cu, q_segs, kv_segs, q_bits, k_bits, v_bits, hq, hkv, d, scale, poison=True):
+    """One sap_attn_fwd call; q_bits are local Q rows, k/v_bits local KV rows."""
+    import torch
+    plan = sap.sap_plan(cu, q_segs, kv_segs, 128, 64)
+    info = sap.sap_plan_info(plan)
+    tq = info["tq"]
+    q = to_dev(q_bits)
+    k = to_dev(k_bits)
+    v = to_dev(v_bits)
+    o = torch.full((tq, hq, d), float("nan") if poison else 0.0, device="cuda")
+    lse = torch.full((hq, tq), float("nan") if poison else 0.0, device="cuda")
+    if info["n_tiles"]:
+        sap.sap_plan_upload(plan)
+    sap.sap_attn_fwd(plan, q, k, v, q.stride(0), k.stride(0), hq, hkv, d, scale, o, lse)
+    torch.cuda.synchronize()
+    touched, desc = sap.sap_plan_q_tiles(plan)
+    rows = np.array([r for t in touched for r in range(desc[t, 0], desc[t, 0] + desc[t, 1])], dtype=np.int64)
+    return o.cpu().numpy(), lse.cpu().numpy(), rows, info
+
+
+def _globals(segs, n):
+    g = np.full(n, -1, dtype=np.int64)
+    for gs, ge, ls in segs:
+        g[ls:ls + ge - gs] = np.arange(gs, ge)
+    return g
+
+
+def test_tiny_full_sequence():
+    sap = _sap()
+    w = W.tiny()
+    t = tensors("tiny")
+    say("case tiny_packed_512: one call, Q = KV = 512 tokens, D=64")
+    o, lse, rows, info = _run_single(sap, w.cu, w.q_segs, w.steps[0].kv_segs, t.q, t.k, t.v, 2, 2, 64, w.scale)
+    assert info["n_tiles"] == 11 and len(rows) == 512
+    g = np.arange(512)
+    ro, rl = A.forward(f64(t.q), f64(t.k), f64(t.v), g, g, w.cu, w.scale)
+    compare(o, lse, ro, rl, label="tiny")
+    # error against the unrounded fp32 inputs is reported, not gated
+    q32, k32, v32 = W.fp32_inputs_tiny()
+    fo, _ = A.forward(q32, k32, v32, g, g, w.cu, w.scale)
+    say(f"  tiny vs fp32-input oracle (not gated): max|dO|={np.abs(o - fo).max():.3e}")
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_small_layouts(seed):
+    """Ragged tiles, 1-token and empty documents, GQA, D in {64, 128},
+    non-contiguous segments, strided Q rows; untouched rows stay NaN."""
+    sap = _sap()
+    rng = np.random.default_rng(900 + seed)
+    d = 128 if seed % 2 else 64
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 3]))
+    total = int(rng.integers(300, 1400))
+    lengths = W.random_docs(rng, total, int(rng.integers(2, 500)))
+    cu = W.cu_seqlens(lengths)
+    a, b = sorted(rng.integers(0, total, size=2).tolist())
+    b = max(b, a + 1)
+    q_segs = [(a, b, 3), (0, min(a, 150), b - a + 10)] if a > 0 else [(a, b, 0)]
+    q_segs = [s for s in q_segs if s[1] > s[0]]
+    c0 = int(rng.integers(0, total))
+    kv_segs = [(c0, total, 0), (0, c0, total - c0 + 7)] if c0 > 0 else [(0, total, 0)]
+    say(f"case random seed={seed} total={total} docs={len(lengths)} hq={hq} hkv={hkv} d={d} q={q_segs} kv={kv_segs}")
+    gq = _globals(q_segs, max(ls + ge - gs for gs, ge, ls in q_segs))
+    gk = _globals(kv_segs, max(ls + ge - gs for gs, ge, ls in kv_segs))
+    rs = np.random.default_rng(seed)
+    qf = W.bf16_round(rs.standard_normal((total, hq, d), dtype=np.float32))
+    kf = W.bf16_round(rs.standard_normal((total, hkv, d), dtype=np.float32))
+    vf = W.bf16_round(rs.standard_normal((total, hkv, d), dtype=np.float32))
+    # local buffers; Q gets an extra padding head so its row stride exceeds hq*d
+    ql = np.zeros((len(gq), hq + 1, d), dtype=np.uint16)
+    ql[gq >= 0, :hq] = qf[gq[gq >= 0]]
+    kl = np.zeros((len(gk), hkv, d), dtype=np.uint16)
+    vl = np.zeros((len(gk), hkv, d), dtype=np.uint16)
+    kl[gk >= 0], vl[gk >= 0] = kf[gk[gk >= 0]], vf[gk[gk >= 0]]
+    import torch
+    plan = sap.sap_plan(cu, q_segs, kv_segs, 128, 64)
+    info = sap.sap_plan_info(plan)
+    qd, kd, vd = to_dev(ql), to_dev(kl), to_dev(vl)
+    o = torch.full((info["tq"], hq, d), float("nan"), device="cuda")
+    lse = torch.full((hq, info["tq"]), float("nan"), device="cuda")
+    if info["n_tiles"]:
+        sap.sap_plan_upload(plan)
+    sap.sap_attn_fwd(plan, qd, kd, vd, qd.stride(0), kd.stride(0), hq, hkv, d, 1.0 / np.sqrt(d), o, lse)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    touched, desc = sap.sap_plan_q_tiles(plan)
+    rows = np.array([r for t in touched for r in range(desc[t, 0], desc[t, 0] + desc[t, 1])], dtype=np.int64)
+    valid = np.nonzero(gq >= 0)[0]
+    untouched = np.setdiff1d(np.arange(info["tq"]), rows)
+    assert np.isnan(o[untouched]).all() and np.isnan(lse[:, untouched]).all(), "wrote outside touched tiles"
+    q64 = np.zeros((len(gq), hq, d))
+    q64[valid] = f64(qf[gq[valid]])
+    ro, rl = A.forward(q64, f64(kl), f64(vl), np.where(gq >= 0, gq, 0), np.where(gk >= 0, gk, -10**9), cu,
+                       1.0 / np.sqrt(d), rows=rows)
+    compare(o, lse, ro, rl, rows=rows, label=f"random{seed}")
+
+
+def test_forward_is_deterministic():
+    sap = _sap()
+    w = W.ring_rank(3)
+    t = tensors("ring")
+    q_loc = W.local_rows(t.q, w.q_segs)
+    say("case ring rank3 step0 twice (bitwise)")
+    a = _run_single(sap, w.cu, w.q_segs, w.steps[0].kv_segs, q_loc, t.k, t.v, 32, 32, 128, w.scale)
+    b = _run_single(sap, w.cu, w.q_segs, w.steps[0].kv_segs, q_loc, t.k, t.v, 32, 32, 128, w.scale)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def _rank_run(name):
+    import torch
+    from long_context_sequence_doc_amd.rank import RankForward
+    w = W.by_name(name)
+    t = tensors(name)
+    rf = RankForward(w.cu, w.q_segs, [s.kv_segs for s in w.steps], w.hq, w.hkv, w.d, w.scale)
+    q = to_dev(W.local_rows(t.q, w.q_segs))
+    k, v = to_dev(t.k), to_dev(t.v)
+    rf.run(q, k, v, q.stride(0), k.stride(0))
+    torch.cuda.synchronize()
+    return w, t, rf, q, k, v
+
+
+def test_ring_rank_all_steps_and_merge():
+    """32K ring, rank 3: step-by-step partials and the merged result, all rows."""
+    sap = _sap()
+    import torch
+    say("case ring_sp8_32k_rank3: 8 ring steps (2 non-empty) + merge")
+    w, t, rf, q, k, v = _rank_run("ring")
+    assert rf.active == [0, 1]
+    o, lse = rf.o.cpu().numpy(), rf.lse.cpu().numpy()
+    gq = w.q_global_rows()
+    ro, rl = A.forward(f64(W.local_rows(t.q, w.q_segs)), f64(t.k), f64(t.v), gq, np.arange(w.total), w.cu, w.scale)
+    compare(o, lse, ro, rl, label="ring merged")
+    # the non-empty remote step alone
+    s1 = w.steps[1]
+    gk = np.concatenate([np.arange(a, b) for a, b, _ in s1.kv_segs])
+    po, pl = A.forward(f64(W.local_rows(t.q, w.q_segs)), f64(t.k[gk]), f64(t.v[gk]), gq, gk, w.cu, w.scale)
+    rows = np.array(rf.touched_rows(1))
+    compare(rf.o_part.cpu().numpy(), rf.lse_part.cpu().numpy(), po, pl, rows=rows, label="ring step1 partial")
+    rf.close()
+
+
+def test_zigzag_gqa_headline_sampled():
+    """128K zigzag GQA shard (rank 3), the benchmarked configuration; sampled rows."""
+    _sap()
+    say("case zigzag_sp8_128k_gqa_rank3: 3 non-empty steps + 2 merges, sampled rows")
+    w, t, rf, q, k, v = _rank_run("zigzag")
+    assert rf.active == [0, 1, 7]
+    gq = w.q_global_rows()
+    rows = sample_rows(gq, w.cu)
+    ro, rl = A.forward(f64(W.local_rows(t.q, w.q_segs)), f64(t.k), f64(t.v), gq, np.arange(w.total), w.cu, w.scale,
+                       rows=rows)
+    compare(rf.o.cpu().numpy(), rf.lse.cpu().numpy(), ro, rl, rows=rows, label="zigzag merged")
+    rf.close()
+
+
+def test_training_forward_sampled():
+    _sap()
+    say("case train_64k_5heads forward, sampled rows")
+    w, t, rf, q, k, v = _rank_run("train")
+    g = np.arange(w.total)
+    rows = sample_rows(g, w.cu, n_random=512)
+    ro, rl = A.forward(f64(t.q), f64(t.k), f64(t.v), g, g, w.cu, w.scale, rows=rows)
+    compare(rf.o.cpu().numpy(), rf.lse.cpu().numpy(), ro, rl, rows=rows, label="train fwd")
+    rf.close()
+
+
+def test_ulysses_sampled():
+    """512K Ulysses head shard: rows sampled from every document, the end of each long one."""
+    _sap()
+    say("case ulysses_512k_4heads forward, sampled rows")
+    w, t, rf, q, k, v = _rank_run("ulysses")
+    g = np.arange(w.total)
+    cu = w.cu
+    rng = np.random.default_rng(5)
+    rows = set(sample_rows(g, cu, n_random=0).tolist()[::8])
+    for i in (0, 1):
+        s, e = int(cu[i]), int(cu[i + 1])
+        rows.update(range(e - 64, e))
+        rows.update(rng.integers(s, e, size=64).tolist())
+    rows = np.array(sorted(rows))
+    ro, rl = A.forward(f64(t.q), f64(t.k), f64(t.v), g, g, cu, w.scale, rows=rows)
+    compare(rf.o.cpu().numpy(), rf.lse.cpu().numpy(), ro, rl, rows=rows, label="ulysses")
+    rf.close()
+
+
+def test_merge_against_oracle():
+    """sap_lse_merge alone: dense (plan NULL) and plan-restricted, with -inf rows."""
+    sap = _sap()
+    import torch
+    rng = np.random.default_rng(3)
+    tq, hq, d = 300, 3, 64
+    oa = rng.standard_normal((tq, hq, d)).astype(np.float32)
+    ob = rng.standard_normal((tq, hq, d)).astype(np.float32)
+    la = (3 * rng.standard_normal((hq, tq))).astype(np.float32)
+    lb = (3 * rng.standard_normal((hq, tq))).astype(np.float32)
+    la[0, :7] = -np.inf
+    oa[:7, 0] = 0
+    lb[1, 5:12] = -np.inf
+    ob[5:12, 1] = 0
+    la[2, 20:25] = -np.inf
+    lb[2, 20:25] = -np.inf
+    oa[20:25, 2] = 0
+    ob[20:25, 2] = 0
+    say("case merge dense 300x3x64")
+    t = lambda x: torch.from_numpy(x).cuda()
+    da, dla = t(oa), t(la)
+    sap.sap_lse_merge(None, da, dla, t(ob), t(lb), tq, hq, d)
+    torch.cuda.synchronize()
+    ro, rl = A.merge(oa, la, ob, lb)
+    compare(da.cpu().numpy(), dla.cpu().numpy(), ro, rl, label="merge dense")
+    assert np.abs(da.cpu().numpy() - ro).max() < 1e-5
+    # plan-restricted: rows outside touched tiles must be left as they were
+    say("case merge plan-restricted")
+    cu = [0, 200, 300]
+    plan = sap.sap_plan(cu, [(0, 300, 0)], [(200, 300, 0)], 128, 64)   # KV = 2nd doc: touches tiles 1, 2
+    sap.sap_plan_upload(plan)
+    da, dla = t(oa), t(la)
+    sap.sap_lse_merge(plan, da, dla, t(ob), t(lb), tq, hq, d)
+    torch.cuda.synchronize()
+    touched, desc = sap.sap_plan_q_tiles(plan)
+    rows = np.array([r for tt in touched for r in range(desc[tt, 0], desc[tt, 0] + desc[tt, 1])])
+    other = np.setdiff1d(np.arange(tq), rows)
+    got = da.cpu().numpy()
+    assert np.array_equal(got[other], oa[other])
+    assert np.array_equal(dla.cpu().numpy()[:, other], la[:, other])
+    compare(got, dla.cpu().numpy(), ro, rl, rows=rows, label="merge plan rows")
