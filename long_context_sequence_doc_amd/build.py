@@ -4,7 +4,8 @@
 
 Each source is compiled by hipcc for gfx950 into ``_build/`` and linked into
 ``long_context_sequence_doc_amd/libsap.so``. Packed-FP32 instructions are
-disabled for device code (``-packed-fp32-ops``).
+disabled for device code (``-packed-fp32-ops``) and matrix-core results are
+kept in VGPRs (``-amdgpu-mfma-vgpr-form``).
 """
 from __future__ import annotations
 
@@ -25,7 +26,10 @@ SOURCES = ["planner.cpp", "sap_api.cpp", "attn_fwd.hip", "lse_merge.hip", "attn_
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           f"-I{os.path.join(ROOT, 'include')}"]
-DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Matrix-core results go straight to VGPRs (no AGPR staging copies in the
+# softmax loops), and packed-FP32 instructions are disabled.
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def hipcc() -> str:

@@ -91,31 +91,32 @@ struct TileRegs {
   u32x4 vr[VL];
 };
 
+// Global -> register loads of one KV tile. Rows past the tile's end are
+// clamped to its last row (finite values; their scores are masked to -inf and
+// their P is 0), so the loads need no branches. Offsets are 32-bit, relative
+// to the tile's first row of this KV head.
 template <int D>
 __device__ inline void load_tile(TileRegs<D> &r, const FwdParams &p, const PartnerEntry &pe, int g,
                                  int tid) {
   constexpr int CPR = D / 8;                 // 16-byte chunks per K row
   constexpr int RPI = NTHREADS / CPR;        // rows covered per pass
-  const int c = tid % CPR;
   const int64_t base = int64_t(pe.local_start) * p.kv_row_stride + int64_t(g) * D;
+  const unsigned short *kb = p.k + base;
+  const unsigned short *vb = p.v + base;
+  const int stride = int(p.kv_row_stride);
+  const int last = pe.n - 1;
 #pragma unroll
   for (int i = 0; i < TileRegs<D>::KL; ++i) {
-    const int row = tid / CPR + RPI * i;
-    if (row < pe.n)
-      r.kr[i] = *reinterpret_cast<const u32x4 *>(p.k + base + int64_t(row) * p.kv_row_stride + 8 * c);
-    else
-      r.kr[i] = u32x4{0u, 0u, 0u, 0u};
+    const int row = min(tid / CPR + RPI * i, last);
+    r.kr[i] = *reinterpret_cast<const u32x4 *>(kb + row * stride + 8 * (tid % CPR));
   }
   constexpr int KPT = D / 32;                // consecutive keys per thread
   constexpr int NKG = BN / KPT;              // key groups
   const int kg = tid % NKG, dc = tid / NKG;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
-    const int row = kg * KPT + i;
-    if (row < pe.n)
-      r.vr[i] = *reinterpret_cast<const u32x4 *>(p.v + base + int64_t(row) * p.kv_row_stride + 8 * dc);
-    else
-      r.vr[i] = u32x4{0u, 0u, 0u, 0u};
+    const int row = min(kg * KPT + i, last);
+    r.vr[i] = *reinterpret_cast<const u32x4 *>(vb + row * stride + 8 * dc);
   }
 }
 
@@ -216,30 +217,34 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(FwdParams p) {
       load_tile<D>(regs, p, pe, g, tid);
     }
 
-    // S^T for 64 keys x this wave's 32 queries
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      const unsigned short *kp = kbuf + (kb * 32 + l32) * S::KS + 8 * hf;
+    // S^T for 64 keys x this wave's 32 queries: two independent accumulator
+    // chains (key blocks) interleaved so each LDS read is issued ahead of use
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+    {
+      const unsigned short *kp = kbuf + l32 * S::KS + 8 * hf;
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + 16 * t));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kb], 0, 0, 0);
+        const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + 16 * t));
+        const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + 32 * S::KS + 16 * t));
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[t], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[t], s[1], 0, 0, 0);
       }
     }
 
     if (cur.cls != SAP_TILE_FULL || cur.n < BN) {
+      // allowed keys of this lane's query, as tile-local key indices [lo, hi];
+      // element i of key block kb holds key kbase + kb*32 + 8*(i/4) + (i%4)
+      const int kbase = 4 * hf;
+      int hi = cur.n - 1;
+      if (cur.cls != SAP_TILE_FULL) hi = min(hi, qg - cur.global_start);
+      const int lo = cur.cls == SAP_TILE_PARTIAL ? dsq - cur.global_start : 0;
+      const int hi_r = hi - kbase, lo_r = lo - kbase;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = kb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-          const int kg = cur.global_start + key;
-          bool ok = key < cur.n;
-          if (cur.cls != SAP_TILE_FULL) ok = ok && kg <= qg;
-          if (cur.cls == SAP_TILE_PARTIAL) ok = ok && kg >= dsq;
-          s[kb][i] = ok ? s[kb][i] : -INFINITY;
+          const int kc = kb * 32 + 8 * (i >> 2) + (i & 3);
+          s[kb][i] = (kc <= hi_r && kc >= lo_r) ? s[kb][i] : -INFINITY;
         }
     }
 
@@ -280,16 +285,19 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(FwdParams p) {
         pb[kb][u] = as_bf16x8(pk);
       }
 
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const unsigned short *vp = vbuf + (db * 32 + l32) * S::VS + 8 * hf;
+    // O^T += V^T P^T: the D/32 output blocks are independent chains, so the
+    // inner loop over them keeps several MFMAs and LDS reads in flight
+    {
+      const unsigned short *vp = vbuf + l32 * S::VS + 8 * hf;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(vp + kb * 32 + 16 * u));
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][u], oacc[db], 0, 0, 0);
-        }
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(vp + db * 32 * S::VS + kb * 32 + 16 * u));
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][u], oacc[db], 0, 0, 0);
+          }
     }
 
     if (more) store_tile<D>(regs, lds + ((it + 1) & 1) * S::BUF, tid);
@@ -341,7 +349,8 @@ hipError_t launch_attn_fwd(const FwdLaunch &a, hipStream_t stream) {
   p.c = a.scale * LOG2E;
   const int64_t slots = (int64_t(p.n_groups) + NXCD - 1) / NXCD;
   const int64_t blocks = slots * NXCD * p.group;
-  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  // 32-bit row offsets inside a 64-row tile
+  if (blocks > INT32_MAX || a.kv_row_stride > INT32_MAX / BN) return hipErrorInvalidValue;
   const dim3 grid{static_cast<unsigned>(blocks)}, block{NTHREADS};
   if (a.d == 128)
     hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, block, 0, stream, p);
