@@ -41,6 +41,9 @@ def _args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="zigzag", choices=["zigzag", "ring", "ulysses", "train", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="before the run, one plain device-to-device copy of this many MiB (a known-size "
+                         "reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -115,6 +118,13 @@ def main():
     k = torch.from_numpy(t.k.view(np.int16)).view(torch.bfloat16).cuda()
     v = torch.from_numpy(t.v.view(np.int16)).view(torch.bfloat16).cuda()
     stream = torch.cuda.current_stream()
+    if a.calibration_copy_mib:
+        src = torch.empty(a.calibration_copy_mib << 18, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(a.warmup):
         rf.run(q, k, v, q.stride(0), k.stride(0))

@@ -1,10 +1,411 @@
-// Backward kernels (recompute form): placeholder until the gfx950 kernel lands.
+// Backward kernels (recompute form) for document-masked causal attention on
+// gfx950 bf16 matrix cores.
+//
+// The forward keeps only O and the log-sum-exp; the backward recomputes the
+// probabilities from them -- the attention-level echo of the AutoSP page's
+// section 2.B (gist.science/zh/paper/2604.27089: keep attention's saved
+// state, recompute instead of storing the big intermediates). With the
+// final, all-KV LSE and O of each query row:
+//     P = exp(scale q.k - LSE)                  on allowed pairs (else 0)
+//     D_r = dO_r . O_r                          (bwd_preprocess_kernel)
+//     dV += P^T dO,   dS = P o (dO V^T - D),   dK += scale dS^T Q,   dQ += scale dS K
+// so per-step calls of a ring sum to the full gradient.
+//
+// attn_bwd_kernel: one workgroup = one 128-key KV tile x one KV head; 4 waves
+// own 32 keys each. It walks the Q tiles (64 rows) that meet its KV tile
+// (transposed tile list) and, for each, the query heads of its GQA group:
+//   * S = Q K^T and dP = dO V^T with the wave's K / V rows held in registers
+//     as B operands: P and dS come out of the 32x32 accumulators with keys
+//     across lanes and queries across registers, which is exactly the
+//     B-operand layout of dV^T += dO^T P and dK^T += Q^T dS. Q^T and dO^T are
+//     staged in LDS transposed, with the 4-row groups of every 16 query rows
+//     ordered (0-3, 8-11, 4-7, 12-15) to match the accumulator's row order.
+//   * dQ needs dS with keys as the contraction: dS goes through LDS once and
+//     dQ^T = K^T dS^T runs against a transposed copy of the K tile (staged
+//     once per workgroup); each wave produces 32 of the 128 head dims with one
+//     query per lane and adds them to the fp32 dQ buffer with atomics.
+//   * dK / dV stay in registers across all Q tiles and heads, and are added
+//     to the caller's buffers at the end (each (KV tile, KV head) belongs to
+//     exactly one workgroup, so no atomics).
 #include <hip/hip_runtime.h>
+
+#include <cmath>
 
 #include "kernels.h"
 
 namespace sap {
+namespace {
 
-hipError_t launch_attn_bwd(const BwdLaunch &, hipStream_t) { return hipErrorNotSupported; }
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+
+constexpr int BMB = 64;     // query rows per Q tile
+constexpr int BNB = 128;    // keys per KV tile
+constexpr int NT = 256;
+constexpr float LOG2E = 1.4426950408889634f;
+
+__device__ inline bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+__device__ inline unsigned pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+__device__ inline int perm16(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// Four rows' 16-byte chunks (8 columns each) -> for each column j, the four
+// rows' elements packed as two dwords (rows 0,1 | rows 2,3).
+__device__ inline u32x2 gather4(const u32x4 (&r)[4], int j) {
+  const int w = j >> 1;
+  const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
+  u32x2 pk;
+  pk.x = __builtin_amdgcn_perm(r[1][w], r[0][w], sel);
+  pk.y = __builtin_amdgcn_perm(r[3][w], r[2][w], sel);
+  return pk;
+}
+
+// ---------------------------------------------------------------------------
+// D_r = sum_d dO[r,h,d] * O[r,h,d] for the rows of the plan's Q tiles.
+// 32 threads per (row, head); D/32 elements each.
+__global__ __launch_bounds__(NT) void bwd_preprocess_kernel(const unsigned short *dout, int64_t q_row_stride,
+                                                            const float *o, float *delta,
+                                                            const int32_t *tiles, int32_t hq, int32_t d,
+                                                            int32_t tq) {
+  const int r0 = tiles[2 * blockIdx.x], n = tiles[2 * blockIdx.x + 1];
+  const int pair = blockIdx.y * (NT / 32) + threadIdx.x / 32;   // (row, head) index inside the tile
+  const int lane = threadIdx.x & 31;
+  if (pair >= n * hq) return;
+  const int row = r0 + pair / hq, h = pair % hq;
+  const unsigned short *dp = dout + int64_t(row) * q_row_stride + int64_t(h) * d;
+  const float *op = o + (int64_t(row) * hq + h) * d;
+  float acc = 0.f;
+  for (int e = lane; e < d; e += 32) {
+    const float dv = __builtin_bit_cast(float, unsigned(dp[e]) << 16);
+    acc += dv * op[e];
+  }
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 32);
+  if (lane == 0) delta[int64_t(h) * tq + row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+struct BwdParams {
+  const unsigned short *q, *k, *v, *dout;
+  const float *lse, *delta;
+  int64_t q_row_stride, kv_row_stride;
+  float *dq, *dk, *dv;
+  const WorkItem *work;
+  const WorkRange *range;
+  const PartnerEntry *partners;
+  const int32_t *ds_q;
+  int32_t hq, hkv, group, tq, n_work;
+  float scale, c;   // c = scale * log2(e)
+};
+
+template <int D>
+struct BwdSmem {
+  static constexpr int RS = D + 8;            // row-major Q / dO row stride (elements)
+  static constexpr int TS = BMB + 8;          // transposed Q / dO row stride
+  static constexpr int KTS = BNB + 8;         // transposed K row stride
+  static constexpr int SS = BNB + 8;          // dS row stride
+  static constexpr int Q_ROW = 0;
+  static constexpr int DO_ROW = Q_ROW + BMB * RS;
+  static constexpr int Q_T = DO_ROW + BMB * RS;
+  static constexpr int DO_T = Q_T + D * TS;
+  static constexpr int K_T = DO_T + D * TS;
+  static constexpr int DS = K_T + D * KTS;
+  static constexpr int ELEMS = DS + BMB * SS;  // bf16 elements
+};
+
+template <int D>
+__global__ __launch_bounds__(NT) void attn_bwd_kernel(BwdParams p) {
+  using S = BwdSmem<D>;
+  __shared__ __attribute__((aligned(16))) unsigned short lds[S::ELEMS];
+  __shared__ float s_lse2[BMB], s_delta[BMB];
+  __shared__ int s_ds[BMB];
+
+  const int w = blockIdx.x / p.hkv, g = blockIdx.x % p.hkv;
+  if (w >= p.n_work) return;
+  const WorkItem kt = p.work[w];
+  const WorkRange rg = p.range[w];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+
+  // this wave's keys: local key index wave*32 + l32 within the tile
+  const int my_key = wave * 32 + l32;
+  const bool key_ok = my_key < kt.n;
+  const int kg = kt.global_start + my_key;
+  const int64_t kv_base = int64_t(kt.local_start) * p.kv_row_stride + int64_t(g) * D;
+
+  // K / V rows of this lane's key as B operands (8 consecutive d per k-step)
+  bf16x8 kf[D / 16], vf[D / 16];
+  {
+    const int krow = min(my_key, kt.n - 1);
+    const unsigned short *kp = p.k + kv_base + int64_t(krow) * p.kv_row_stride + 8 * hf;
+    const unsigned short *vp = p.v + kv_base + int64_t(krow) * p.kv_row_stride + 8 * hf;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      kf[t] = as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + 16 * t));
+      vf[t] = as_bf16x8(*reinterpret_cast<const u32x4 *>(vp + 16 * t));
+    }
+  }
+  // K^T of the whole tile into LDS (B operand of dQ = dS K): K_T[d][key]
+  {
+    constexpr int NKG = BNB / 4;               // 32 groups of 4 keys
+    constexpr int ITEMS = NKG * (D / 8);
+#pragma unroll
+    for (int ps = 0; ps < (ITEMS + NT - 1) / NT; ++ps) {
+      const int idx = ps * NT + tid;
+      if (ITEMS % NT != 0 && idx >= ITEMS) break;
+      const int kgp = idx % NKG, dc = idx / NKG;
+      u32x4 r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = min(kgp * 4 + i, kt.n - 1);
+        r[i] = *reinterpret_cast<const u32x4 *>(p.k + kv_base + int64_t(row) * p.kv_row_stride + 8 * dc);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<u32x2 *>(lds + S::K_T + (8 * dc + j) * S::KTS + 4 * kgp) = gather4(r, j);
+    }
+  }
+
+  f32x16 dka[D / 32], dva[D / 32];     // dK^T / dV^T blocks: lane = key, registers = d
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    dka[i] = f32x16{};
+    dva[i] = f32x16{};
+  }
+  const float c = p.c;
+
+  for (int it = 0; it < rg.count; ++it) {
+    const PartnerEntry qt = p.partners[rg.begin + it];
+    for (int hi = 0; hi < p.group; ++hi) {
+      const int h = g * p.group + hi;
+      __syncthreads();   // previous iteration done with the Q / dO / dS buffers
+      // ---- stage Q and dO rows: row-major and transposed copies
+      {
+        constexpr int NQG = BMB / 4;           // 16 groups of 4 query rows
+        constexpr int ITEMS = NQG * (D / 8);
+#pragma unroll
+        for (int ps = 0; ps < (ITEMS + NT - 1) / NT; ++ps) {
+          const int idx = ps * NT + tid;
+          if (ITEMS % NT != 0 && idx >= ITEMS) break;
+          const int qgp = idx % NQG, dc = idx / NQG;
+          u32x4 rq[4], rd[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = min(qgp * 4 + i, qt.n - 1);
+            const int64_t off = int64_t(qt.local_start + row) * p.q_row_stride + int64_t(h) * D + 8 * dc;
+            rq[i] = *reinterpret_cast<const u32x4 *>(p.q + off);
+            rd[i] = *reinterpret_cast<const u32x4 *>(p.dout + off);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            *reinterpret_cast<u32x4 *>(lds + S::Q_ROW + (qgp * 4 + i) * S::RS + 8 * dc) = rq[i];
+            *reinterpret_cast<u32x4 *>(lds + S::DO_ROW + (qgp * 4 + i) * S::RS + 8 * dc) = rd[i];
+          }
+          const int col = ((qgp * 4) & ~15) | perm16((qgp * 4) & 15);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            *reinterpret_cast<u32x2 *>(lds + S::Q_T + (8 * dc + j) * S::TS + col) = gather4(rq, j);
+            *reinterpret_cast<u32x2 *>(lds + S::DO_T + (8 * dc + j) * S::TS + col) = gather4(rd, j);
+          }
+        }
+        if (tid < BMB) {
+          const int row = min(tid, qt.n - 1);
+          const int64_t li = int64_t(h) * p.tq + qt.local_start + row;
+          const float l = p.lse[li];
+          // rows past the tile end or with no key at all get P = 0
+          s_lse2[tid] = (tid < qt.n && l != -INFINITY) ? l * LOG2E : INFINITY;
+          s_delta[tid] = p.delta[li];
+          s_ds[tid] = p.ds_q[qt.local_start + row];
+        }
+      }
+      __syncthreads();
+
+      // ---- S = Q K^T, dP = dO V^T (64 queries x this wave's 32 keys)
+      f32x16 sacc[2], pacc[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        sacc[qb] = f32x16{};
+        pacc[qb] = f32x16{};
+      }
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const int row = qb * 32 + l32;
+          const bf16x8 aq = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + S::Q_ROW + row * S::RS + 16 * t + 8 * hf));
+          const bf16x8 ad = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + S::DO_ROW + row * S::RS + 16 * t + 8 * hf));
+          sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[t], sacc[qb], 0, 0, 0);
+          pacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[t], pacc[qb], 0, 0, 0);
+        }
+
+      // ---- P and dS; accumulator element i of block qb is query row
+      //      qb*32 + 8*(i/4) + 4*hf + (i%4), key my_key
+      const bool masked = qt.cls != SAP_TILE_FULL || qt.n < BMB || kt.n < BNB;
+      bf16x8 pb[2][2], sb[2][2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          float pv[8], sv[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int i = 8 * u + j;
+            const int r = qb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
+            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][i], c, -s_lse2[r]));
+            if (masked) {
+              const int qg = qt.global_start + r;
+              bool ok = key_ok && kg <= qg;
+              if (qt.cls == SAP_TILE_PARTIAL) ok = ok && kg >= s_ds[r];
+              pr = ok ? pr : 0.f;
+            }
+            pv[j] = pr;
+            sv[j] = pr * (pacc[qb][i] - s_delta[r]);
+          }
+          u32x4 pk, sk;
+          pk.x = pack_bf16(pv[0], pv[1]);
+          pk.y = pack_bf16(pv[2], pv[3]);
+          pk.z = pack_bf16(pv[4], pv[5]);
+          pk.w = pack_bf16(pv[6], pv[7]);
+          sk.x = pack_bf16(sv[0], sv[1]);
+          sk.y = pack_bf16(sv[2], sv[3]);
+          sk.z = pack_bf16(sv[4], sv[5]);
+          sk.w = pack_bf16(sv[6], sv[7]);
+          pb[qb][u] = as_bf16x8(pk);
+          sb[qb][u] = as_bf16x8(sk);
+        }
+
+      // ---- dV^T += dO^T P, dK^T += Q^T dS (k = 16 query rows per step)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const int off = (db * 32 + l32) * S::TS + qb * 32 + 16 * u + 8 * hf;
+            const bf16x8 ado = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + S::DO_T + off));
+            const bf16x8 aqt = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + S::Q_T + off));
+            dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, pb[qb][u], dva[db], 0, 0, 0);
+            dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, sb[qb][u], dka[db], 0, 0, 0);
+          }
+
+      // ---- dS -> LDS as [query][key] (bf16); element i of block qb is row
+      //      qb*32 + 8*(i/4) + 4*hf + (i%4): one base address + constant offsets
+      {
+        unsigned short *dsp = lds + S::DS + (4 * hf) * S::SS + my_key;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const u32x4 sk = __builtin_bit_cast(u32x4, sb[qb][u]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const int i = 8 * u + j;
+              const unsigned word = sk[j >> 1];
+              dsp[(qb * 32 + 8 * (i >> 2) + (i & 3)) * S::SS] =
+                  static_cast<unsigned short>((j & 1) ? (word >> 16) : (word & 0xffffu));
+            }
+          }
+      }
+      __syncthreads();
+
+      // ---- dQ^T[wave's 32 dims][64 queries] = K^T dS^T (k = 128 keys):
+      //      lane = query, registers = dims, so each lane adds into one dQ row
+      if (wave < D / 32) {
+        f32x16 qacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+        for (int t = 0; t < BNB / 16; ++t) {
+          const bf16x8 ak = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + S::K_T + (wave * 32 + l32) * S::KTS + 16 * t + 8 * hf));
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            const bf16x8 bs = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + S::DS + (qb * 32 + l32) * S::SS + 16 * t + 8 * hf));
+            qacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, bs, qacc[qb], 0, 0, 0);
+          }
+        }
+        // accumulator: row = d wave*32 + 8*(i/4) + 4*hf + (i%4), column = query qb*32 + l32
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const int r = qb * 32 + l32;
+          if (r < qt.n) {
+            float *dqp = p.dq + (int64_t(qt.local_start + r) * p.hq + h) * D + wave * 32 + 4 * hf;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) unsafeAtomicAdd(dqp + 8 * (i >> 2) + (i & 3), qacc[qb][i] * p.scale);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- dK += scale dK^T, dV += dV^T for this wave's keys
+  if (!key_ok) return;
+  float *dkp = p.dk + (int64_t(kt.local_start + my_key) * p.hkv + g) * D + 4 * hf;
+  float *dvp = p.dv + (int64_t(kt.local_start + my_key) * p.hkv + g) * D + 4 * hf;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int ig = 0; ig < 4; ++ig) {
+      const int off = db * 32 + 8 * ig;
+      f32x4 a = *reinterpret_cast<f32x4 *>(dkp + off);
+      f32x4 b = *reinterpret_cast<f32x4 *>(dvp + off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] += p.scale * dka[db][4 * ig + e];
+        b[e] += dva[db][4 * ig + e];
+      }
+      *reinterpret_cast<f32x4 *>(dkp + off) = a;
+      *reinterpret_cast<f32x4 *>(dvp + off) = b;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd(const BwdLaunch &a, hipStream_t stream) {
+  if (a.n_touched_q > 65535 || a.n_work > INT32_MAX / a.hkv) return hipErrorInvalidValue;
+  // D_r for every row of the plan's touched Q tiles
+  {
+    const int pairs = a.max_q_rows * a.hq;
+    const dim3 grid{static_cast<unsigned>(a.n_touched_q), static_cast<unsigned>((pairs + NT / 32 - 1) / (NT / 32))};
+    hipLaunchKernelGGL(bwd_preprocess_kernel, grid, dim3(NT), 0, stream,
+                       static_cast<const unsigned short *>(a.dout), a.q_row_stride, a.o, a.delta, a.touched_rows,
+                       a.hq, a.d, a.tq);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  BwdParams p;
+  p.q = static_cast<const unsigned short *>(a.q);
+  p.k = static_cast<const unsigned short *>(a.k);
+  p.v = static_cast<const unsigned short *>(a.v);
+  p.dout = static_cast<const unsigned short *>(a.dout);
+  p.lse = a.lse;
+  p.delta = a.delta;
+  p.q_row_stride = a.q_row_stride;
+  p.kv_row_stride = a.kv_row_stride;
+  p.dq = a.dq;
+  p.dk = a.dk;
+  p.dv = a.dv;
+  p.work = a.work;
+  p.range = a.range;
+  p.partners = a.partners;
+  p.ds_q = a.ds_q;
+  p.hq = a.hq;
+  p.hkv = a.hkv;
+  p.group = a.hq / a.hkv;
+  p.tq = a.tq;
+  p.n_work = a.n_work;
+  p.scale = a.scale;
+  p.c = a.scale * LOG2E;
+  const dim3 grid{static_cast<unsigned>(a.n_work * a.hkv)};
+  if (a.d == 128)
+    hipLaunchKernelGGL(attn_bwd_kernel<128>, grid, dim3(NT), 0, stream, p);
+  else
+    hipLaunchKernelGGL(attn_bwd_kernel<64>, grid, dim3(NT), 0, stream, p);
+  return hipGetLastError();
+}
 
 }  // namespace sap

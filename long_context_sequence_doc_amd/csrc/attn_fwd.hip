@@ -91,32 +91,49 @@ struct TileRegs {
   u32x4 vr[VL];
 };
 
-// Global -> register loads of one KV tile. Rows past the tile's end are
-// clamped to its last row (finite values; their scores are masked to -inf and
-// their P is 0), so the loads need no branches. Offsets are 32-bit, relative
-// to the tile's first row of this KV head.
+// Per-thread element offsets of the KV tile loads, relative to the tile's
+// first row of the KV head; loop-invariant for full 64-row tiles.
 template <int D>
-__device__ inline void load_tile(TileRegs<D> &r, const FwdParams &p, const PartnerEntry &pe, int g,
-                                 int tid) {
+struct LoadOffsets {
+  int k[D / 32];
+  int v[D / 32];
+};
+
+template <int D>
+__device__ inline LoadOffsets<D> load_offsets(int stride, int tid, int rows) {
   constexpr int CPR = D / 8;                 // 16-byte chunks per K row
   constexpr int RPI = NTHREADS / CPR;        // rows covered per pass
+  constexpr int KPT = D / 32;                // consecutive keys per thread (V)
+  constexpr int NKG = BN / KPT;              // key groups
+  LoadOffsets<D> o;
+  const int last = rows - 1;
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) o.k[i] = min(tid / CPR + RPI * i, last) * stride + 8 * (tid % CPR);
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) o.v[i] = min((tid % NKG) * KPT + i, last) * stride + 8 * (tid / NKG);
+  return o;
+}
+
+// Global -> register loads of one KV tile. Rows past a short tile's end are
+// clamped to its last row (finite values; their scores are masked to -inf and
+// their P is 0), so the loads need no per-row branches.
+template <int D>
+__device__ inline void load_tile(TileRegs<D> &r, const FwdParams &p, const PartnerEntry &pe, int g,
+                                 int tid, const LoadOffsets<D> &full) {
   const int64_t base = int64_t(pe.local_start) * p.kv_row_stride + int64_t(g) * D;
   const unsigned short *kb = p.k + base;
   const unsigned short *vb = p.v + base;
-  const int stride = int(p.kv_row_stride);
-  const int last = pe.n - 1;
+  if (pe.n == BN) {
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::KL; ++i) {
-    const int row = min(tid / CPR + RPI * i, last);
-    r.kr[i] = *reinterpret_cast<const u32x4 *>(kb + row * stride + 8 * (tid % CPR));
-  }
-  constexpr int KPT = D / 32;                // consecutive keys per thread
-  constexpr int NKG = BN / KPT;              // key groups
-  const int kg = tid % NKG, dc = tid / NKG;
+    for (int i = 0; i < D / 32; ++i) r.kr[i] = *reinterpret_cast<const u32x4 *>(kb + full.k[i]);
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int row = min(kg * KPT + i, last);
-    r.vr[i] = *reinterpret_cast<const u32x4 *>(vb + row * stride + 8 * dc);
+    for (int i = 0; i < D / 32; ++i) r.vr[i] = *reinterpret_cast<const u32x4 *>(vb + full.v[i]);
+  } else {
+    const LoadOffsets<D> o = load_offsets<D>(int(p.kv_row_stride), tid, pe.n);
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) r.kr[i] = *reinterpret_cast<const u32x4 *>(kb + o.k[i]);
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) r.vr[i] = *reinterpret_cast<const u32x4 *>(vb + o.v[i]);
   }
 }
 
@@ -156,9 +173,13 @@ __device__ inline void store_tile(const TileRegs<D> &r, unsigned short *buf, int
 
 __device__ inline bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// two fp32 -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
 __device__ inline unsigned pack_bf16(float lo, float hi) {
-  __bf16 a = static_cast<__bf16>(lo), b = static_cast<__bf16>(hi);
-  return unsigned(__builtin_bit_cast(unsigned short, a)) | (unsigned(__builtin_bit_cast(unsigned short, b)) << 16);
+  const bf16x2 v = __builtin_convertvector(f32x2{lo, hi}, bf16x2);
+  return __builtin_bit_cast(unsigned, v);
 }
 
 template <int D>
@@ -201,9 +222,10 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(FwdParams p) {
   const float c = p.c;
 
   TileRegs<D> regs;
+  const LoadOffsets<D> full_offs = load_offsets<D>(int(p.kv_row_stride), tid, BN);
   const PartnerEntry *pes = p.partners + rg.begin;
   PartnerEntry pe = pes[0];
-  load_tile<D>(regs, p, pe, g, tid);
+  load_tile<D>(regs, p, pe, g, tid, full_offs);
   store_tile<D>(regs, lds, tid);
   __syncthreads();
 
@@ -214,7 +236,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(FwdParams p) {
     const bool more = it + 1 < rg.count;
     if (more) {
       pe = pes[it + 1];
-      load_tile<D>(regs, p, pe, g, tid);
+      load_tile<D>(regs, p, pe, g, tid, full_offs);
     }
 
     // S^T for 64 keys x this wave's 32 queries: two independent accumulator

@@ -133,7 +133,7 @@ def merge(o_a, lse_a, o_b, lse_b):
     return o, lse
 
 
-def backward(q, k, v, do, o_final, lse_final, gq, gk, cu, scale):
+def backward(q, k, v, do, o_final, lse_final, gq, gk, cu, scale, rows=None, cols=None):
     """Gradients of this call's share of sum(O * dO) (recompute form).
 
     O_final / LSE_final are the merged results over *all* KV rows of the
@@ -148,8 +148,28 @@ def backward(q, k, v, do, o_final, lse_final, gq, gk, cu, scale):
         dQ[r,h] += scale sum_c dS_rc k[c,g]
         dK[c,g] += scale sum_{h in g} sum_r dS_rc q[r,h]
 
+    ``rows`` / ``cols``: optional subsets of local Q rows / KV rows. Every
+    dQ row is a sum over keys and every dK/dV row a sum over queries, each
+    independent of the others, so with a subset the oracle computes dQ for
+    ``rows`` only (against all keys) and dK/dV for ``cols`` only (against all
+    queries); the rest stay 0. Without subsets it is one pass over all pairs.
+
     Returns dq [Tq,Hq,D], dk [Tkv,Hkv,D], dv [Tkv,Hkv,D] (fp64).
     """
+    if rows is not None or cols is not None:
+        all_r = np.arange(np.asarray(q).shape[0])
+        all_c = np.arange(np.asarray(k).shape[0])
+        r_sel = all_r if rows is None else np.asarray(rows, dtype=np.int64)
+        c_sel = all_c if cols is None else np.asarray(cols, dtype=np.int64)
+        dq, _, _ = _backward_pairs(q, k, v, do, o_final, lse_final, gq, gk, cu, scale, r_sel, all_c)
+        _, dk, dv = _backward_pairs(q, k, v, do, o_final, lse_final, gq, gk, cu, scale, all_r, c_sel)
+        return dq, dk, dv
+    return _backward_pairs(q, k, v, do, o_final, lse_final, gq, gk, cu, scale, None, None)
+
+
+def _backward_pairs(q, k, v, do, o_final, lse_final, gq, gk, cu, scale, rows, cols):
+    """The backward sums of ``backward`` over query rows ``rows`` x key rows
+    ``cols`` (None = all)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -165,8 +185,10 @@ def backward(q, k, v, do, o_final, lse_final, gq, gk, cu, scale):
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     delta = np.einsum("thd,thd->ht", do, o_final)
-    rows = np.arange(tq)
+    rows = np.arange(tq) if rows is None else rows
     for qrows, kcols in _doc_groups(cu, gq, gk, rows):
+        if cols is not None:
+            kcols = np.intersect1d(kcols, cols)
         if len(kcols) == 0:
             continue
         for qb in _blocks(qrows, len(kcols)):

@@ -117,3 +117,21 @@ def test_ring_steps_sum_to_full_gradient(rng):
     assert np.abs(sq - dq).max() < 1e-12
     assert np.abs(sk - dk).max() < 1e-12
     assert np.abs(sv - dv).max() < 1e-12
+
+
+def test_sampled_rows_and_cols_are_exact(rng):
+    """dQ rows and dK/dV rows are independent sums; the sampled form matches."""
+    lengths = [40, 1, 70, 17]
+    hq, hkv, d, scale = 4, 2, 8, 0.35
+    q, k, v, do, cu = _inputs(rng, lengths, hq, hkv, d)
+    (dq, dk, dv), o, lse = _full(q, k, v, do, cu, scale)
+    g = np.arange(q.shape[0])
+    rows = np.array([0, 39, 40, 41, 100, 127])
+    cols = np.array([3, 40, 55, 110, 111])
+    sq, sk, sv = A.backward(q, k, v, do, o, lse, g, g, cu, scale, rows=rows, cols=cols)
+    assert np.abs(sq[rows] - dq[rows]).max() < 1e-13
+    assert np.abs(sk[cols] - dk[cols]).max() < 1e-13
+    assert np.abs(sv[cols] - dv[cols]).max() < 1e-13
+    other_r = np.setdiff1d(g, rows)
+    other_c = np.setdiff1d(g, cols)
+    assert (sq[other_r] == 0).all() and (sk[other_c] == 0).all() and (sv[other_c] == 0).all()
