@@ -1,0 +1,188 @@
+"""GPU parity of the backward (bwd_preprocess + attn_bwd) against the fp64 oracle.
+
+The backward consumes the final O and LSE; the small cases feed the GPU the
+oracle's O / LSE (rounded to fp32) to test the backward in isolation, the
+full-size training case the GPU forward's (as a training step would) while
+the oracle runs its own forward. dQ / dK / dV
+are compared max-abs within 2e-2 (bf16 inputs; P and dS rounded to bf16 for
+the matrix cores; fp32 accumulation). Every call goes through the C ABI.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention as A
+from tests.gpu_common import TOL_O, f64, need_gpu, say, tensors, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _sap():
+    need_gpu()
+    import long_context_sequence_doc_amd as sap
+    return sap
+
+
+def _globals(segs, n):
+    g = np.full(n, -1, dtype=np.int64)
+    for gs, ge, ls in segs:
+        g[ls:ls + ge - gs] = np.arange(gs, ge)
+    return g
+
+
+def _check(name, got, ref, rows=None):
+    got = np.asarray(got, dtype=np.float64)
+    if rows is not None:
+        got, ref = got[rows], ref[rows]
+    assert not np.isnan(got).any(), f"{name}: NaN"
+    err = float(np.abs(got - ref).max()) if ref.size else 0.0
+    say(f"  {name}: max|err|={err:.3e} (max|ref|={np.abs(ref).max():.2e})")
+    assert err <= TOL_O, f"{name}: {err}"
+
+
+def _bwd_call(sap, cu, q_segs, kv_segs, qd, kd, vd, dod, o, lse, hq, hkv, d, scale, dq, dk, dv):
+    import torch
+    plan = sap.sap_plan(cu, q_segs, kv_segs, 64, 128)
+    info = sap.sap_plan_info(plan)
+    if info["n_tiles"]:
+        sap.sap_plan_upload(plan)
+    ws_bytes = sap.sap_attn_bwd_workspace(plan, hq, d)
+    ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")
+    sap.sap_attn_bwd(plan, qd, kd, vd, o, lse, dod, qd.stride(0), kd.stride(0), hq, hkv, d, scale,
+                     dq, dk, dv, ws, ws.numel() * 4)
+    return plan, ws          # the caller keeps both alive until the stream is synchronised
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_small_layouts(seed):
+    """Ragged tiles, 1-token and empty documents, GQA, D in {64, 128}, a
+    sharded Q (two segments, local != global rows) and KV in two pieces."""
+    sap = _sap()
+    import torch
+    rng = np.random.default_rng(700 + seed)
+    d = 128 if seed % 2 else 64
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 4]))
+    total = int(rng.integers(200, 900))
+    lengths = W.random_docs(rng, total, int(rng.integers(2, 400)))
+    cu = W.cu_seqlens(lengths)
+    a = int(rng.integers(0, total - 1))
+    q_segs = [(a, total, 5), (0, a, total - a + 9)] if a > 0 else [(0, total, 0)]
+    c0 = int(rng.integers(0, total))
+    kv_segs = [(c0, total, 0), (0, c0, total - c0 + 3)] if c0 > 0 else [(0, total, 0)]
+    say(f"case bwd random seed={seed} total={total} docs={len(lengths)} hq={hq} hkv={hkv} d={d}")
+    scale = 1.0 / np.sqrt(d)
+    gq = _globals(q_segs, max(ls + ge - gs for gs, ge, ls in q_segs))
+    gk = _globals(kv_segs, max(ls + ge - gs for gs, ge, ls in kv_segs))
+    rs = np.random.default_rng(seed)
+    mk = lambda h: W.bf16_round(rs.standard_normal((total, h, d), dtype=np.float32))
+    qf, kf, vf, dof = mk(hq), mk(hkv), mk(hkv), mk(hq)
+    ql = np.zeros((len(gq), hq, d), dtype=np.uint16)
+    dol = np.zeros((len(gq), hq, d), dtype=np.uint16)
+    kl = np.zeros((len(gk), hkv, d), dtype=np.uint16)
+    vl = np.zeros((len(gk), hkv, d), dtype=np.uint16)
+    vq, vk = gq >= 0, gk >= 0
+    ql[vq], dol[vq] = qf[gq[vq]], dof[gq[vq]]
+    kl[vk], vl[vk] = kf[gk[vk]], vf[gk[vk]]
+    gq0 = np.where(vq, gq, 0)
+    gk0 = np.where(vk, gk, -10 ** 9)
+    # final O / LSE from the oracle over this call's KV (= all keys here)
+    o_ref, lse_ref = A.forward(f64(ql), f64(kl), f64(vl), gq0, gk0, cu, scale)
+    rows = np.nonzero(vq)[0]
+    dq_ref, dk_ref, dv_ref = A.backward(f64(ql), f64(kl), f64(vl), f64(dol), o_ref, lse_ref, gq0, gk0, cu, scale)
+    qd, kd, vd, dod = to_dev(ql), to_dev(kl), to_dev(vl), to_dev(dol)
+    o = torch.from_numpy(o_ref.astype(np.float32)).cuda()
+    lse = torch.from_numpy(lse_ref.astype(np.float32)).cuda()
+    dq = torch.zeros((len(gq), hq, d), device="cuda")
+    dk = torch.zeros((len(gk), hkv, d), device="cuda")
+    dv = torch.zeros((len(gk), hkv, d), device="cuda")
+    keep = _bwd_call(sap, cu, q_segs, kv_segs, qd, kd, vd, dod, o, lse, hq, hkv, d, scale, dq, dk, dv)
+    torch.cuda.synchronize()
+    del keep                                      # plans are freed only after the kernels finished
+    _check("dQ", dq.cpu().numpy(), dq_ref, rows)
+    kr = np.nonzero(vk)[0]
+    _check("dK", dk.cpu().numpy(), dk_ref, kr)
+    _check("dV", dv.cpu().numpy(), dv_ref, kr)
+    # rows outside every segment were never touched
+    assert (dq.cpu().numpy()[~vq] == 0).all() and (dk.cpu().numpy()[~vk] == 0).all()
+
+
+def test_ring_steps_accumulate_to_full_gradient():
+    """Per-step calls with the final LSE add up (dq/dk/dv are accumulated)."""
+    sap = _sap()
+    import torch
+    rng = np.random.default_rng(11)
+    total, hq, hkv, d = 768, 4, 2, 128
+    lengths = W.random_docs(rng, total, 300)
+    cu = W.cu_seqlens(lengths)
+    scale = 1.0 / np.sqrt(d)
+    mk = lambda h: W.bf16_round(rng.standard_normal((total, h, d), dtype=np.float32))
+    qf, kf, vf, dof = mk(hq), mk(hkv), mk(hkv), mk(hq)
+    g = np.arange(total)
+    q_segs = [(256, 512, 0)]                      # the rank's rows
+    gq = np.arange(256, 512)
+    o_ref, lse_ref = A.forward(f64(qf[256:512]), f64(kf), f64(vf), gq, g, cu, scale)
+    dq_ref, dk_ref, dv_ref = A.backward(f64(qf[256:512]), f64(kf), f64(vf), f64(dof[256:512]), o_ref, lse_ref,
+                                        gq, g, cu, scale)
+    qd, dod = to_dev(qf[256:512]), to_dev(dof[256:512])
+    kd, vd = to_dev(kf), to_dev(vf)
+    o = torch.from_numpy(o_ref.astype(np.float32)).cuda()
+    lse = torch.from_numpy(lse_ref.astype(np.float32)).cuda()
+    dq = torch.zeros((256, hq, d), device="cuda")
+    dk = torch.zeros((total, hkv, d), device="cuda")
+    dv = torch.zeros((total, hkv, d), device="cuda")
+    say("case bwd ring: 3 KV chunks of 256, accumulated")
+    keep = []
+    for c in range(3):
+        keep.append(_bwd_call(sap, cu, q_segs, [(256 * c, 256 * (c + 1), 256 * c)], qd, kd, vd, dod, o, lse,
+                              hq, hkv, d, scale, dq, dk, dv))
+    torch.cuda.synchronize()
+    del keep
+    _check("dQ ring", dq.cpu().numpy(), dq_ref)
+    _check("dK ring", dk.cpu().numpy(), dk_ref)
+    _check("dV ring", dv.cpu().numpy(), dv_ref)
+
+
+def test_training_fwd_bwd_sampled():
+    """64K training sequence (5 heads, 30 documents incl. 1-token ones):
+    GPU forward then GPU backward; sampled dQ rows and dK/dV rows vs the oracle."""
+    sap = _sap()
+    import torch
+    from long_context_sequence_doc_amd.rank import RankForward
+    w = W.training()
+    t = tensors("train", True)
+    say("case train_64k_5heads fwd+bwd, sampled rows")
+    rf = RankForward(w.cu, w.q_segs, [s.kv_segs for s in w.steps], w.hq, w.hkv, w.d, w.scale)
+    qd, kd, vd, dod = to_dev(t.q), to_dev(t.k), to_dev(t.v), to_dev(t.do)
+    o, lse = rf.run(qd, kd, vd, qd.stride(0), kd.stride(0))
+    dq = torch.zeros((w.total, w.hq, w.d), device="cuda")
+    dk = torch.zeros_like(dq)
+    dv = torch.zeros_like(dq)
+    keep = _bwd_call(sap, w.cu, w.q_segs, w.steps[0].kv_segs, qd, kd, vd, dod, o, lse, w.hq, w.hkv, w.d,
+                     w.scale, dq, dk, dv)
+    torch.cuda.synchronize()
+    del keep
+    g = np.arange(w.total)
+    rng = np.random.default_rng(5)
+    cu = w.cu
+    # dQ rows: seeded random rows, document starts (1-token documents included), the end
+    pick = set(rng.integers(0, w.total, size=96).tolist())
+    for s0 in cu[:-1].tolist():
+        pick.update((s0, min(w.total - 1, s0 + 1)))
+    pick.update(range(w.total - 8, w.total))
+    rows = np.array(sorted(pick))
+    # dK/dV rows: the last 3 keys of every document, so only a few queries see them
+    cols = np.array(sorted({c for e in cu[1:].tolist() for c in range(max(0, e - 3), e)}))
+    # the oracle's own forward, on every query row those gradients depend on
+    need = set(rows.tolist())
+    for c in cols.tolist():
+        e = int(cu[np.searchsorted(cu, c, side="right")])
+        need.update(range(c, e))
+    need = np.array(sorted(need))
+    o_ref, lse_ref = A.forward(f64(t.q), f64(t.k), f64(t.v), g, g, cu, w.scale, rows=need)
+    dq_ref, dk_ref, dv_ref = A.backward(f64(t.q), f64(t.k), f64(t.v), f64(t.do), o_ref, lse_ref, g, g, cu,
+                                        w.scale, rows=rows, cols=cols)
+    _check("dQ train", dq.cpu().numpy(), dq_ref, rows)
+    _check("dK train", dk.cpu().numpy(), dk_ref, cols)
+    _check("dV train", dv.cpu().numpy(), dv_ref, cols)
+    rf.close()
