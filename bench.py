@@ -1,17 +1,20 @@
 """Benchmark: one sequence-parallel rank's document-masked attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload zigzag|ring|ulysses|train|tiny]
-                    [--no-cpu-baseline]
+                    [--forward-only] [--no-cpu-baseline]
 
-A step is one pass of the rank's hot path over resident inputs: for the
-default 128K zigzag GQA shard (131072-token packed sequence, SP degree 8,
+A step is one pass of the rank's whole hot path over resident inputs: for
+the default 128K zigzag GQA shard (131072-token packed sequence, SP degree 8,
 rank 3 holds 16384 query rows, 32 query / 8 KV heads, head_dim 128) that is
-the forward of every non-empty ring step plus the exact LSE merges. Plans are
-built once, outside the timed region. Prints ONE JSON line.
+the forward of every non-empty ring step with the exact LSE merges, then the
+recompute backward (row terms once, one accumulate call per non-empty step)
+with the final O and LSE. Plans are built once, outside the timed region.
+Prints ONE JSON line.
 
 Throughput counts only allowed (unmasked) query-key pairs: 4 * head_dim FLOP
-per pair per query head for the forward. The roofline object prices the
-dominant kernel (attn_fwd) against the bf16 dense matrix-core peak, using the
+per pair per query head for the forward and 10 * head_dim for the backward
+(recompute of Q K^T and dO V^T, then dV, dK, dQ). The roofline object prices
+the dominant kernel against the bf16 dense matrix-core peak, using that
 kernel's own launch durations measured with HIP events on its stream.
 
 The CPU baseline times the fp64 oracle (test infrastructure) on a bounded
@@ -41,6 +44,8 @@ def _args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="zigzag", choices=["zigzag", "ring", "ulysses", "train", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="time only the forward ring steps and merges (no backward)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before the run, one plain device-to-device copy of this many MiB (a known-size "
                          "reference for HBM byte counters)")
@@ -61,10 +66,13 @@ def _traffic_from_profiles(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, t, budget_s: float = 20.0):
-    """The oracle, as it stands, on a bounded sample: one KV head group's query
-    heads over every ring step, all local rows of this rank. Rate = the
-    sample's allowed-pair FLOP / wall time."""
+def cpu_baseline(w, t, forward_only: bool, budget_s: float = 30.0):
+    """The oracle, as it stands, on a bounded sample of the same workload: the
+    query heads of KV head 0 over this rank's rows, every non-empty ring step
+    (forward per step; then, unless forward-only, the oracle forward over all
+    KV rows for the final O / LSE and the backward per step). Rate = the
+    sample's allowed-pair FLOP (4 D forward + 10 D backward per pair and
+    query head) / wall time."""
     from oracle import attention as A
     from oracle import planner as P
     import workloads as W
@@ -73,30 +81,64 @@ def cpu_baseline(w, t, budget_s: float = 20.0):
         cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         cores = 1
-    group = w.hq // w.hkv
-    heads = list(range(group))           # query heads of KV head 0
+    heads = list(range(w.hq // w.hkv))           # query heads of KV head 0
     q = W.bf16_to_f32(W.local_rows(t.q, w.q_segs)[:, heads]).astype(np.float64)
     k = W.bf16_to_f32(t.k[:, :1]).astype(np.float64)
     v = W.bf16_to_f32(t.v[:, :1]).astype(np.float64)
     gq = w.q_global_rows()
-    pairs = 0
+    pairs, steps_done, flop = 0, 0, 0.0
     t0 = time.perf_counter()
-    steps_done = 0
+    steps = []
     for st in w.steps:
         gk = np.concatenate([np.arange(a, b) for a, b, _ in st.kv_segs])
         pl = P.plan(w.cu, w.q_segs, st.kv_segs, 128, 64)
         if pl.n_tiles == 0:
             continue
         A.forward(q, k[gk], v[gk], gq, gk, w.cu, w.scale)
-        pairs += pl.useful_pairs
+        flop += 4.0 * w.d * len(heads) * pl.useful_pairs
+        steps.append((gk, pl.useful_pairs))
         steps_done += 1
         if time.perf_counter() - t0 > budget_s:
             break
+    bwd_steps = 0
+    if not forward_only:
+        do = W.bf16_to_f32(W.local_rows(t.do, w.q_segs)[:, heads]).astype(np.float64)
+        allk = np.arange(w.total)
+        t1 = time.perf_counter()
+        o, lse = A.forward(q, k, v, gq, allk, w.cu, w.scale)
+        t0 += time.perf_counter() - t1      # the final O / LSE are inputs here, not timed work
+        for gk, pr in steps:
+            A.backward(q, k[gk], v[gk], do, o, lse, gq, gk, w.cu, w.scale)
+            flop += 10.0 * w.d * len(heads) * pr
+            bwd_steps += 1
     dt = time.perf_counter() - t0
-    flop = 4.0 * w.d * len(heads) * pairs
+    what = "forward per step" if forward_only else \
+        f"forward per step, then backward for {bwd_steps} steps from the oracle's final O/LSE (not timed)"
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{w.name}: query heads 0-{len(heads) - 1} (KV head 0), all {w.tq} local rows, "
-                      f"{steps_done} non-empty ring steps; fp64 NumPy; {dt:.1f} s wall"}
+                      f"{steps_done} non-empty ring steps ({what}); fp64 NumPy; {dt:.1f} s wall"}
+
+
+class _Timer:
+    """HIP events bracketing launches on one stream, grouped by kernel."""
+
+    def __init__(self, stream):
+        import torch
+        self.torch, self.stream, self.ev = torch, stream, {}
+
+    def run(self, name, fn):
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        fn()
+        e1.record(self.stream)
+        self.ev.setdefault(name, []).append((e0, e1))
+
+    def ms(self, name):
+        return sum(a.elapsed_time(b) for a, b in self.ev.get(name, []))
+
+    def count(self, name):
+        return len(self.ev.get(name, []))
 
 
 def main():
@@ -107,16 +149,25 @@ def main():
     import torch
     import workloads as W
     import long_context_sequence_doc_amd as sap
-    from long_context_sequence_doc_amd.rank import RankForward
+    from long_context_sequence_doc_amd.rank import RankBackward, RankForward
 
     w = W.by_name(a.workload)
-    t = W.make_tensors(w)
+    fwd_only = a.forward_only
+    t = W.make_tensors(w, with_do=not fwd_only)
     t_plan0 = time.perf_counter()
-    rf = RankForward(w.cu, w.q_segs, [s.kv_segs for s in w.steps], w.hq, w.hkv, w.d, w.scale)
+    kv_steps = [s.kv_segs for s in w.steps]
+    rf = RankForward(w.cu, w.q_segs, kv_steps, w.hq, w.hkv, w.d, w.scale)
+    rb = None if fwd_only else RankBackward(w.cu, w.q_segs, kv_steps, w.hq, w.hkv, w.d, w.scale)
     plan_s = time.perf_counter() - t_plan0
-    q = torch.from_numpy(W.local_rows(t.q, w.q_segs).view(np.int16)).view(torch.bfloat16).cuda()
-    k = torch.from_numpy(t.k.view(np.int16)).view(torch.bfloat16).cuda()
-    v = torch.from_numpy(t.v.view(np.int16)).view(torch.bfloat16).cuda()
+    dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    q = dev(W.local_rows(t.q, w.q_segs))
+    k, v = dev(t.k), dev(t.v)
+    if not fwd_only:
+        dout = dev(W.local_rows(t.do, w.q_segs))
+        # gradient buffers are zeroed once; the timed steps keep accumulating into them
+        dq = torch.zeros((rf.tq, w.hq, w.d), dtype=torch.float32, device="cuda")
+        dk = torch.zeros((k.shape[0], w.hkv, w.d), dtype=torch.float32, device="cuda")
+        dv = torch.zeros_like(dk)
     stream = torch.cuda.current_stream()
     if a.calibration_copy_mib:
         src = torch.empty(a.calibration_copy_mib << 18, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -126,46 +177,71 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    qs, ks = q.stride(0), k.stride(0)
+
+    def step(tm):
+        for n, i in enumerate(rf.active):
+            if n == 0:
+                tm.run("attn_fwd", lambda: sap.sap_attn_fwd(rf.plans[i], q, k, v, qs, ks, w.hq, w.hkv, w.d,
+                                                            w.scale, rf.o, rf.lse))
+            else:
+                tm.run("attn_fwd", lambda: sap.sap_attn_fwd(rf.plans[i], q, k, v, qs, ks, w.hq, w.hkv, w.d,
+                                                            w.scale, rf.o_part, rf.lse_part))
+                tm.run("lse_merge", lambda: sap.sap_lse_merge(rf.plans[i], rf.o, rf.lse, rf.o_part, rf.lse_part,
+                                                              rf.tq, w.hq, w.d))
+        if rb is not None:
+            tm.run("bwd_rowterm", lambda: rb.rowterm(rf.o, dout, qs))
+            for i in rb.active:
+                tm.run("attn_bwd", lambda: rb.accumulate(i, q, k, v, rf.lse, dout, qs, ks, dq, dk, dv))
+
+    warm = _Timer(stream)
     for _ in range(a.warmup):
-        rf.run(q, k, v, q.stride(0), k.stride(0))
+        step(warm)
     torch.cuda.synchronize()
 
-    # timed region; the forward launches are bracketed by events on their stream
-    fwd_events = []
-    merge_events = []
+    tm = _Timer(stream)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for _ in range(a.steps):
-        for n, i in enumerate(rf.active):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            out_o, out_l = (rf.o, rf.lse) if n == 0 else (rf.o_part, rf.lse_part)
-            e0.record(stream)
-            sap.sap_attn_fwd(rf.plans[i], q, k, v, q.stride(0), k.stride(0), w.hq, w.hkv, w.d, w.scale,
-                             out_o, out_l)
-            e1.record(stream)
-            fwd_events.append((e0, e1))
-            if n > 0:
-                m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                m0.record(stream)
-                sap.sap_lse_merge(rf.plans[i], rf.o, rf.lse, rf.o_part, rf.lse_part, rf.tq, w.hq, w.d)
-                m1.record(stream)
-                merge_events.append((m0, m1))
+        step(tm)
     end.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / a.steps
-    fwd_ms = sum(e0.elapsed_time(e1) for e0, e1 in fwd_events)
-    merge_ms = sum(e0.elapsed_time(e1) for e0, e1 in merge_events)
+    ms_per_step = start.elapsed_time(end) / a.steps
 
-    flop = rf.useful_flop
+    fwd_flop = rf.useful_flop
+    bwd_flop = 0.0 if rb is None else rb.useful_flop
+    flop = fwd_flop + bwd_flop
     value = flop / (ms_per_step * 1e-3) / 1e12
-    n_fwd = len(fwd_events)
-    fwd_avg_ms = fwd_ms / max(n_fwd, 1)
-    flop_per_launch = flop * a.steps / max(n_fwd, 1)
-    achieved = flop_per_launch / (fwd_avg_ms * 1e-3) / 1e12 if n_fwd else 0.0
+
+    def kernel_stats(name, flop_per_step):
+        n = tm.count(name)
+        if not n:
+            return None
+        ms = tm.ms(name)
+        avg = ms / n
+        ach = flop_per_step * a.steps / (ms * 1e-3) / 1e12
+        return {"launches_per_step": n // a.steps, "avg_launch_ms": round(avg, 4), "ms_per_step": round(ms / a.steps, 4),
+                "tflops": round(ach, 3), "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+
+    fwd = kernel_stats("attn_fwd", fwd_flop)
+    bwd = kernel_stats("attn_bwd", bwd_flop) if rb is not None else None
+    dom_name, dom, dom_flop = ("attn_fwd", fwd, fwd_flop)
+    if bwd is not None and bwd["ms_per_step"] > fwd["ms_per_step"]:
+        dom_name, dom, dom_flop = ("attn_bwd", bwd, bwd_flop)
     merge_bytes = rf.merge_rows() * (12 * w.d + 12)
-    merge_gbs = (merge_bytes * a.steps / (merge_ms * 1e-3) / 1e9) if merge_events else None
-    traffic = _traffic_from_profiles("attn_fwd", w.name)
+    merge = None
+    if tm.count("lse_merge"):
+        gbs = merge_bytes * a.steps / (tm.ms("lse_merge") * 1e-3) / 1e9
+        merge = {"bound": "hbm", "achieved_gbs": round(gbs, 1), "peak_gbs": PEAK_HBM_GBS,
+                 "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_step": merge_bytes,
+                 "avg_launch_ms": round(tm.ms("lse_merge") / tm.count("lse_merge"), 4)}
+    rowterm = None
+    if tm.count("bwd_rowterm"):
+        # dO (bf16) + O (fp32) read, D written, per (row, head)
+        rt_bytes = rf.tq * w.hq * (6 * w.d + 4)
+        gbs = rt_bytes * a.steps / (tm.ms("bwd_rowterm") * 1e-3) / 1e9
+        rowterm = {"bound": "hbm", "achieved_gbs": round(gbs, 1), "peak_gbs": PEAK_HBM_GBS,
+                   "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_step": rt_bytes}
 
     line = {
         "metric": "Effective TFLOP/s (unmasked pairs only) + % of bf16 MFMA peak, 128K packed",
@@ -183,6 +259,7 @@ def main():
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "config": {
             "workload": w.name,
+            "step": "forward (ring steps + LSE merges)" + ("" if fwd_only else " + recompute backward"),
             "seq_len": w.total,
             "documents": len(w.lengths),
             "q_rows": w.tq,
@@ -193,28 +270,28 @@ def main():
             "nonempty_steps": len(rf.active),
             "useful_pairs_per_head": rf.useful_pairs_per_head,
             "useful_flop_per_step": flop,
-            "tile": [128, 64],
+            "flop_per_pair_per_head": 4 * w.d if fwd_only else 14 * w.d,
+            "tiles": {"forward": [128, 64], "backward": [64, 128]},
             "plan_host_s": round(plan_s, 3),
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_fwd",
-            "achieved": round(achieved, 3),
+            "kernel": dom_name,
+            "achieved": dom["tflops"],
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic,
-            "launches_per_step": n_fwd // a.steps,
-            "avg_launch_ms": round(fwd_avg_ms, 4),
+            "frac": dom["frac"],
+            "traffic": _traffic_from_profiles(dom_name, w.name),
+            "launches_per_step": dom["launches_per_step"],
+            "avg_launch_ms": dom["avg_launch_ms"],
         },
-        "merge": None if merge_gbs is None else {
-            "bound": "hbm", "achieved_gbs": round(merge_gbs, 1), "peak_gbs": PEAK_HBM_GBS,
-            "frac": round(merge_gbs / PEAK_HBM_GBS, 4), "bytes_per_step": merge_bytes,
-            "avg_launch_ms": round(merge_ms / len(merge_events), 4)},
+        "kernels": {"attn_fwd": fwd, "attn_bwd": bwd, "lse_merge": merge, "bwd_rowterm": rowterm},
     }
     if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, t)
+        line["cpu_baseline"] = cpu_baseline(w, t, fwd_only)
     rf.close()
+    if rb is not None:
+        rb.close()
     print(json.dumps(line), flush=True)
 
 

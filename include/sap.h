@@ -187,6 +187,30 @@ sap_status sap_attn_bwd(sap_plan_t plan, const void *q, const void *k, const voi
                         float *dq, float *dk, float *dv,
                         void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/*
+ * sap_attn_bwd_rowterm -- the backward's row terms D_r = dO_r . O_r (O the
+ * final merged forward output) for the rows of the plan's touched Q tiles,
+ * into delta fp32 [Hq][Tq] (device; other rows untouched). HBM-bound.
+ * A ring rank computes them once with the plan of its own chunk (which
+ * touches every local row) and reuses them for every step's
+ * sap_attn_bwd_accumulate. Plan tile shape 64 x 128.
+ */
+sap_status sap_attn_bwd_rowterm(sap_plan_t plan, const float *o, const void *dout,
+                                int64_t q_row_stride, int32_t hq, int32_t d,
+                                float *delta, void *hip_stream);
+
+/*
+ * sap_attn_bwd_accumulate -- sap_attn_bwd without the row-term pass: the
+ * caller passes delta fp32 [Hq][Tq] from sap_attn_bwd_rowterm (it must hold
+ * the rows of this plan's touched Q tiles). Same outputs and accumulation
+ * rules as sap_attn_bwd. Plan tile shape 64 x 128.
+ */
+sap_status sap_attn_bwd_accumulate(sap_plan_t plan, const void *q, const void *k, const void *v,
+                                   const float *lse_final, const float *delta, const void *dout,
+                                   int64_t q_row_stride, int64_t kv_row_stride,
+                                   int32_t hq, int32_t hkv, int32_t d, float scale,
+                                   float *dq, float *dk, float *dv, void *hip_stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char *sap_last_error(void);
 

@@ -7,7 +7,7 @@ tensors are accepted for device buffers (their data pointers are passed) and
 torch's current stream is used when no stream is given.
 
 There is no fallback: if ``libsap.so`` is missing the import of this package
-fails loudly; build it with ``python -m long_context_sequence_doc_amd.build``.
+fails loudly; build it with ``python long_context_sequence_doc_amd/build.py``.
 """
 from __future__ import annotations
 
@@ -20,6 +20,7 @@ __all__ = [
     "SapError", "Segment", "PlanStats", "Plan",
     "sap_plan", "sap_plan_upload", "sap_plan_info", "sap_plan_tiles", "sap_plan_q_tiles",
     "sap_plan_free", "sap_attn_fwd", "sap_lse_merge", "sap_attn_bwd_workspace", "sap_attn_bwd",
+    "sap_attn_bwd_rowterm", "sap_attn_bwd_accumulate",
     "sap_last_error", "sap_version", "lib_path", "SAP_TILE_FULL", "SAP_TILE_DIAGONAL",
     "SAP_TILE_PARTIAL",
 ]
@@ -31,7 +32,7 @@ _STATUS = {0: "SAP_OK", 1: "SAP_ERR_INVALID_ARG", 2: "SAP_ERR_UNSUPPORTED", 3: "
 
 lib_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsap.so")
 if not os.path.exists(lib_path):
-    raise ImportError(f"{lib_path} is not built; run `python -m long_context_sequence_doc_amd.build`")
+    raise ImportError(f"{lib_path} is not built; run `python long_context_sequence_doc_amd/build.py`")
 _lib = ctypes.CDLL(lib_path)
 
 
@@ -73,6 +74,9 @@ _sigs = {
     "sap_attn_bwd_workspace": ([_P, _i32, _i32], _sz),
     "sap_attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _i64, _i64, _i32, _i32, _i32, _f32, _P, _P, _P, _P, _sz, _P],
                      _i32),
+    "sap_attn_bwd_rowterm": ([_P, _P, _P, _i64, _i32, _i32, _P, _P], _i32),
+    "sap_attn_bwd_accumulate": ([_P, _P, _P, _P, _P, _P, _P, _i64, _i64, _i32, _i32, _i32, _f32, _P, _P, _P, _P],
+                                _i32),
     "sap_last_error": ([], ctypes.c_char_p),
     "sap_version": ([], _i32),
 }
@@ -206,3 +210,15 @@ def sap_attn_bwd(plan: Plan, q, k, v, o, lse_final, dout, q_row_stride: int, kv_
     _check(_lib.sap_attn_bwd(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_final), _ptr(dout),
                              q_row_stride, kv_row_stride, hq, hkv, d, scale, _ptr(dq), _ptr(dk), _ptr(dv),
                              _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def sap_attn_bwd_rowterm(plan: Plan, o, dout, q_row_stride: int, hq: int, d: int, delta, stream=None):
+    _check(_lib.sap_attn_bwd_rowterm(plan.handle, _ptr(o), _ptr(dout), q_row_stride, hq, d, _ptr(delta),
+                                     _stream(stream)))
+
+
+def sap_attn_bwd_accumulate(plan: Plan, q, k, v, lse_final, delta, dout, q_row_stride: int, kv_row_stride: int,
+                            hq: int, hkv: int, d: int, scale: float, dq, dk, dv, stream=None):
+    _check(_lib.sap_attn_bwd_accumulate(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(lse_final), _ptr(delta),
+                                        _ptr(dout), q_row_stride, kv_row_stride, hq, hkv, d, scale, _ptr(dq),
+                                        _ptr(dk), _ptr(dv), _stream(stream)))

@@ -1,6 +1,6 @@
 """Builds libsap.so (host planner, C ABI and gfx950 HIP kernels) in-tree.
 
-    python -m long_context_sequence_doc_amd.build [--verbose] [--resource-usage]
+    python long_context_sequence_doc_amd/build.py [--verbose] [--resource-usage]
 
 Each source is compiled by hipcc for gfx950 into ``_build/`` and linked into
 ``long_context_sequence_doc_amd/libsap.so``. Packed-FP32 instructions are

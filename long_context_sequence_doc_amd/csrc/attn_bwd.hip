@@ -22,8 +22,11 @@
 //     ordered (0-3, 8-11, 4-7, 12-15) to match the accumulator's row order.
 //   * dQ needs dS with keys as the contraction: dS goes through LDS once and
 //     dQ^T = K^T dS^T runs against a transposed copy of the K tile (staged
-//     once per workgroup); each wave produces 32 of the 128 head dims with one
-//     query per lane and adds them to the fp32 dQ buffer with atomics.
+//     once per workgroup); each wave produces 32 of the 128 head dims. The
+//     partial dQ tile is staged in LDS as [query][dim] so the fp32 atomics
+//     into the caller's dQ are row-contiguous (one cache line per 32 lanes),
+//     and each workgroup starts its walk at a different Q tile so the
+//     workgroups sharing Q tiles do not queue on the same rows.
 //   * dK / dV stay in registers across all Q tiles and heads, and are added
 //     to the caller's buffers at the end (each (KV tile, KV head) belongs to
 //     exactly one workgroup, so no atomics).
@@ -119,6 +122,10 @@ struct BwdSmem {
   static constexpr int K_T = DO_T + D * TS;
   static constexpr int DS = K_T + D * KTS;
   static constexpr int ELEMS = DS + BMB * SS;  // bf16 elements
+  // the dQ staging tile [64][QS] fp32 (row padded against bank conflicts)
+  // reuses the Q / dO row buffers, which are dead by then
+  static constexpr int QS = D + 4;
+  static_assert(BMB * QS * 4 <= 2 * BMB * RS * 2, "dQ staging does not fit in the Q / dO row buffers");
 };
 
 template <int D>
@@ -181,8 +188,12 @@ __global__ __launch_bounds__(NT) void attn_bwd_kernel(BwdParams p) {
   }
   const float c = p.c;
 
+  // workgroups of neighbouring KV tiles share Q tiles: start each at a
+  // different partner so their dQ atomics do not queue on the same rows
+  const int rot = int((uint32_t(kt.tile) * 2654435761u) % uint32_t(rg.count));
   for (int it = 0; it < rg.count; ++it) {
-    const PartnerEntry qt = p.partners[rg.begin + it];
+    const int pi = it + rot < rg.count ? it + rot : it + rot - rg.count;
+    const PartnerEntry qt = p.partners[rg.begin + pi];
     for (int hi = 0; hi < p.group; ++hi) {
       const int h = g * p.group + hi;
       __syncthreads();   // previous iteration done with the Q / dO / dS buffers
@@ -328,15 +339,29 @@ __global__ __launch_bounds__(NT) void attn_bwd_kernel(BwdParams p) {
             qacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, bs, qacc[qb], 0, 0, 0);
           }
         }
-        // accumulator: row = d wave*32 + 8*(i/4) + 4*hf + (i%4), column = query qb*32 + l32
+        // accumulator: row = d wave*32 + 8*(i/4) + 4*hf + (i%4), column = query
+        // qb*32 + l32 -> [query][d] fp32 staging in the (now dead) Q / dO row buffers
+        float *stage = reinterpret_cast<float *>(lds + S::Q_ROW);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const int r = qb * 32 + l32;
-          if (r < qt.n) {
-            float *dqp = p.dq + (int64_t(qt.local_start + r) * p.hq + h) * D + wave * 32 + 4 * hf;
+        for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) unsafeAtomicAdd(dqp + 8 * (i >> 2) + (i & 3), qacc[qb][i] * p.scale);
+          for (int ig = 0; ig < 4; ++ig) {
+            f32x4 v4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v4[e] = qacc[qb][4 * ig + e] * p.scale;
+            *reinterpret_cast<f32x4 *>(stage + (qb * 32 + l32) * S::QS + wave * 32 + 8 * ig + 4 * hf) = v4;
           }
+      }
+      __syncthreads();
+      // ---- row-contiguous atomics: consecutive threads add consecutive dims of one row
+      {
+        const float *stage = reinterpret_cast<const float *>(lds + S::Q_ROW);
+        float *dq_tile = p.dq + (int64_t(qt.local_start) * p.hq + h) * D;
+        const int64_t row_stride = int64_t(p.hq) * D;
+#pragma unroll 4
+        for (int e = tid; e < BMB * D; e += NT) {
+          const int r = e / D, dd = e % D;
+          if (r < qt.n) unsafeAtomicAdd(dq_tile + r * row_stride + dd, stage[r * S::QS + dd]);
         }
       }
     }
@@ -365,18 +390,18 @@ __global__ __launch_bounds__(NT) void attn_bwd_kernel(BwdParams p) {
 
 }  // namespace
 
+hipError_t launch_bwd_rowterm(const BwdLaunch &a, hipStream_t stream) {
+  if (a.n_touched_q > 65535) return hipErrorInvalidValue;
+  const int pairs = a.max_q_rows * a.hq;
+  const dim3 grid{static_cast<unsigned>(a.n_touched_q), static_cast<unsigned>((pairs + NT / 32 - 1) / (NT / 32))};
+  hipLaunchKernelGGL(bwd_preprocess_kernel, grid, dim3(NT), 0, stream,
+                     static_cast<const unsigned short *>(a.dout), a.q_row_stride, a.o, a.delta, a.touched_rows,
+                     a.hq, a.d, a.tq);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_bwd(const BwdLaunch &a, hipStream_t stream) {
-  if (a.n_touched_q > 65535 || a.n_work > INT32_MAX / a.hkv) return hipErrorInvalidValue;
-  // D_r for every row of the plan's touched Q tiles
-  {
-    const int pairs = a.max_q_rows * a.hq;
-    const dim3 grid{static_cast<unsigned>(a.n_touched_q), static_cast<unsigned>((pairs + NT / 32 - 1) / (NT / 32))};
-    hipLaunchKernelGGL(bwd_preprocess_kernel, grid, dim3(NT), 0, stream,
-                       static_cast<const unsigned short *>(a.dout), a.q_row_stride, a.o, a.delta, a.touched_rows,
-                       a.hq, a.d, a.tq);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  if (a.n_work > INT32_MAX / a.hkv) return hipErrorInvalidValue;
   BwdParams p;
   p.q = static_cast<const unsigned short *>(a.q);
   p.k = static_cast<const unsigned short *>(a.k);

@@ -43,7 +43,7 @@ struct BwdLaunch {
   int32_t hq, hkv, d;
   float scale;
   float *dq, *dk, *dv;
-  float *delta;                 // workspace [hq][tq]
+  float *delta;                 // row terms [hq][tq]
   int32_t tq;
   const int32_t *touched_rows;  // Q tiles of the plan: (local_start, n) pairs
   int32_t n_touched_q;
@@ -55,6 +55,9 @@ struct BwdLaunch {
   int32_t n_work;
 };
 
+// D_r = dO_r . O_r for the rows of the given tiles
+hipError_t launch_bwd_rowterm(const BwdLaunch &a, hipStream_t stream);
+// dq / dk / dv given a.delta
 hipError_t launch_attn_bwd(const BwdLaunch &a, hipStream_t stream);
 
 }  // namespace sap

@@ -259,37 +259,112 @@ size_t sap_attn_bwd_workspace(sap_plan_t plan, int32_t hq, int32_t d) {
   return align_up(size_t(hq) * size_t(std::max(plan->p.tq, 1)) * sizeof(float));
 }
 
+namespace {
+
+sap_status check_bwd_common(sap_plan_t plan, int32_t hq, int32_t hkv, int32_t d) {
+  if (!plan) return fail(SAP_ERR_INVALID_ARG, "plan is NULL");
+  sap_status s = check_heads(hq, hkv, d);
+  if (s != SAP_OK) return s;
+  if (plan->p.bm != 64 || plan->p.bn != 128) return fail(SAP_ERR_UNSUPPORTED, "backward needs a 64 x 128 plan");
+  return SAP_OK;
+}
+
+void fill_bwd(const sap::Plan &P, sap::BwdLaunch *a) {
+  a->tq = P.tq;
+  a->touched_rows = P.dev.touched_rows;
+  a->n_touched_q = int32_t(P.touched.size());
+  a->max_q_rows = P.bm;
+  a->work = P.dev.kv_work;
+  a->range = P.dev.kv_range;
+  a->partners = P.dev.kv_partners;
+  a->ds_q = P.dev.ds_q;
+  a->n_work = int32_t(P.kv_work.size());
+}
+
+sap_status rowterm_impl(sap_plan_t plan, const float *o, const void *dout, int64_t q_row_stride, int32_t hq,
+                        int32_t d, float *delta, hipStream_t stream) {
+  const sap::Plan &P = plan->p;
+  if (P.touched.empty()) return ok();
+  sap_status s = check_uploaded(plan);
+  if (s != SAP_OK) return s;
+  if (!o || !dout || !delta) return fail(SAP_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(o) || !aligned16(dout) || !aligned16(delta)) return fail(SAP_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (q_row_stride < int64_t(hq) * d || q_row_stride % 8) return fail(SAP_ERR_INVALID_ARG, "q_row_stride must be >= hq*d and a multiple of 8");
+  sap::BwdLaunch a{};
+  a.o = o; a.dout = dout; a.q_row_stride = q_row_stride; a.hq = hq; a.d = d; a.delta = delta;
+  fill_bwd(P, &a);
+  hipError_t e = sap::launch_bwd_rowterm(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "bwd row-term launch");
+  return SAP_OK;
+}
+
+sap_status accumulate_impl(sap_plan_t plan, const void *q, const void *k, const void *v, const float *lse_final,
+                           const float *delta, const void *dout, int64_t q_row_stride, int64_t kv_row_stride,
+                           int32_t hq, int32_t hkv, int32_t d, float scale, float *dq, float *dk, float *dv,
+                           hipStream_t stream) {
+  const sap::Plan &P = plan->p;
+  if (!(scale > 0.f) || !(scale < 1e30f)) return fail(SAP_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (P.kv_work.empty()) return ok();
+  sap_status s = check_uploaded(plan);
+  if (s != SAP_OK) return s;
+  if (!q || !k || !v || !lse_final || !delta || !dout || !dq || !dk || !dv) return fail(SAP_ERR_INVALID_ARG, "NULL pointer");
+  const void *ptrs[] = {q, k, v, lse_final, delta, dout, dq, dk, dv};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return fail(SAP_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (q_row_stride < int64_t(hq) * d || q_row_stride % 8) return fail(SAP_ERR_INVALID_ARG, "q_row_stride must be >= hq*d and a multiple of 8");
+  if (kv_row_stride < int64_t(hkv) * d || kv_row_stride % 8) return fail(SAP_ERR_INVALID_ARG, "kv_row_stride must be >= hkv*d and a multiple of 8");
+  sap::BwdLaunch a{};
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.lse = lse_final; a.delta = const_cast<float *>(delta);
+  a.q_row_stride = q_row_stride; a.kv_row_stride = kv_row_stride;
+  a.hq = hq; a.hkv = hkv; a.d = d; a.scale = scale;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  fill_bwd(P, &a);
+  hipError_t e = sap::launch_attn_bwd(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "attn_bwd launch");
+  return SAP_OK;
+}
+
+}  // namespace
+
+sap_status sap_attn_bwd_rowterm(sap_plan_t plan, const float *o, const void *dout, int64_t q_row_stride,
+                                int32_t hq, int32_t d, float *delta, void *hip_stream) {
+  sap_status s = check_bwd_common(plan, hq, 1, d);
+  if (s != SAP_OK) return s;
+  if ((s = rowterm_impl(plan, o, dout, q_row_stride, hq, d, delta, static_cast<hipStream_t>(hip_stream))) != SAP_OK)
+    return s;
+  return ok();
+}
+
+sap_status sap_attn_bwd_accumulate(sap_plan_t plan, const void *q, const void *k, const void *v,
+                                   const float *lse_final, const float *delta, const void *dout,
+                                   int64_t q_row_stride, int64_t kv_row_stride, int32_t hq, int32_t hkv,
+                                   int32_t d, float scale, float *dq, float *dk, float *dv, void *hip_stream) {
+  sap_status s = check_bwd_common(plan, hq, hkv, d);
+  if (s != SAP_OK) return s;
+  if ((s = accumulate_impl(plan, q, k, v, lse_final, delta, dout, q_row_stride, kv_row_stride, hq, hkv, d, scale,
+                           dq, dk, dv, static_cast<hipStream_t>(hip_stream))) != SAP_OK)
+    return s;
+  return ok();
+}
+
 sap_status sap_attn_bwd(sap_plan_t plan, const void *q, const void *k, const void *v, const float *o,
                         const float *lse_final, const void *dout, int64_t q_row_stride,
                         int64_t kv_row_stride, int32_t hq, int32_t hkv, int32_t d, float scale,
                         float *dq, float *dk, float *dv, void *workspace, size_t workspace_bytes,
                         void *hip_stream) {
-  if (!plan) return fail(SAP_ERR_INVALID_ARG, "plan is NULL");
-  sap_status s = check_heads(hq, hkv, d);
+  sap_status s = check_bwd_common(plan, hq, hkv, d);
   if (s != SAP_OK) return s;
-  const sap::Plan &P = plan->p;
-  if (P.bm != 64 || P.bn != 128) return fail(SAP_ERR_UNSUPPORTED, "backward needs a 64 x 128 plan");
   if (!(scale > 0.f) || !(scale < 1e30f)) return fail(SAP_ERR_INVALID_ARG, "scale must be positive and finite");
-  if (P.kv_work.empty()) return ok();
-  if ((s = check_uploaded(plan)) != SAP_OK) return s;
-  if (!q || !k || !v || !o || !lse_final || !dout || !dq || !dk || !dv || !workspace)
-    return fail(SAP_ERR_INVALID_ARG, "NULL pointer");
-  const void *ptrs[] = {q, k, v, o, lse_final, dout, dq, dk, dv, workspace};
-  for (const void *p : ptrs)
-    if (!aligned16(p)) return fail(SAP_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (plan->p.kv_work.empty()) return ok();
+  if (!workspace) return fail(SAP_ERR_INVALID_ARG, "workspace is NULL");
   if (workspace_bytes < sap_attn_bwd_workspace(plan, hq, d)) return fail(SAP_ERR_INVALID_ARG, "workspace too small");
-  if (q_row_stride < int64_t(hq) * d || q_row_stride % 8) return fail(SAP_ERR_INVALID_ARG, "q_row_stride must be >= hq*d and a multiple of 8");
-  if (kv_row_stride < int64_t(hkv) * d || kv_row_stride % 8) return fail(SAP_ERR_INVALID_ARG, "kv_row_stride must be >= hkv*d and a multiple of 8");
-  sap::BwdLaunch a{};
-  a.q = q; a.k = k; a.v = v; a.dout = dout; a.o = o; a.lse = lse_final;
-  a.q_row_stride = q_row_stride; a.kv_row_stride = kv_row_stride;
-  a.hq = hq; a.hkv = hkv; a.d = d; a.scale = scale;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.delta = static_cast<float *>(workspace); a.tq = P.tq;
-  a.touched_rows = P.dev.touched_rows; a.n_touched_q = int32_t(P.touched.size()); a.max_q_rows = P.bm;
-  a.work = P.dev.kv_work; a.range = P.dev.kv_range; a.partners = P.dev.kv_partners; a.ds_q = P.dev.ds_q;
-  a.n_work = int32_t(P.kv_work.size());
-  hipError_t e = sap::launch_attn_bwd(a, static_cast<hipStream_t>(hip_stream));
-  if (e != hipSuccess) return hip_fail(e, "attn_bwd launch");
+  if (!o) return fail(SAP_ERR_INVALID_ARG, "NULL pointer");
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  float *delta = static_cast<float *>(workspace);
+  if ((s = rowterm_impl(plan, o, dout, q_row_stride, hq, d, delta, stream)) != SAP_OK) return s;
+  if ((s = accumulate_impl(plan, q, k, v, lse_final, delta, dout, q_row_stride, kv_row_stride, hq, hkv, d, scale,
+                           dq, dk, dv, stream)) != SAP_OK)
+    return s;
   return ok();
 }
 

@@ -17,6 +17,10 @@ one rank's work is:
 
 A head-sharded (Ulysses) rank is the one-step case with Q = KV = the whole
 sequence for its heads.
+
+The backward (RankBackward) runs the recompute-based backward once per
+non-empty step with the final O and LSE; the per-step dQ / dK / dV add up to
+the full gradient.
 """
 from __future__ import annotations
 
@@ -24,8 +28,8 @@ from typing import List, Sequence, Tuple
 
 import torch
 
-from . import (sap_attn_fwd, sap_lse_merge, sap_plan, sap_plan_free, sap_plan_info, sap_plan_q_tiles,
-               sap_plan_upload)
+from . import (sap_attn_bwd_accumulate, sap_attn_bwd_rowterm, sap_attn_fwd, sap_lse_merge, sap_plan,
+               sap_plan_free, sap_plan_info, sap_plan_q_tiles, sap_plan_upload)
 
 BLOCK_M, BLOCK_N = 128, 64
 
@@ -84,6 +88,60 @@ class RankForward:
                              self.o_part, self.lse_part, stream)
                 sap_lse_merge(p, self.o, self.lse, self.o_part, self.lse_part, self.tq, self.hq, self.d, stream)
         return self.o, self.lse
+
+    def close(self):
+        for p in self.plans:
+            sap_plan_free(p)
+        self.plans = []
+
+
+class RankBackward:
+    """The rank's backward, given the final (merged) O and LSE:
+        sap_attn_bwd_rowterm once, with the plan of the rank's own chunk (it
+        touches every local row): D_r = dO_r . O_r;
+        sap_attn_bwd_accumulate per non-empty ring step, adding that step's
+        share into the caller's dq / dk / dv (zeroed by the caller once per
+        training step); the shares sum to the full gradient."""
+
+    BLOCK_M, BLOCK_N = 64, 128
+
+    def __init__(self, cu_seqlens, q_segs: Sequence[Tuple[int, int, int]],
+                 step_kv_segs: List[Sequence[Tuple[int, int, int]]], hq: int, hkv: int, d: int,
+                 scale: float, device: str = "cuda"):
+        self.hq, self.hkv, self.d, self.scale = hq, hkv, d, scale
+        self.plans = [sap_plan(cu_seqlens, q_segs, kv, self.BLOCK_M, self.BLOCK_N) for kv in step_kv_segs]
+        self.infos = [sap_plan_info(p) for p in self.plans]
+        first = self.infos[0]
+        if first["n_touched_q_tiles"] != first["n_q_tiles"]:
+            raise ValueError("step 0 must hold the rank's own chunks (it has to touch every local Q tile)")
+        self.tq = first["tq"]
+        self.active = [i for i, inf in enumerate(self.infos) if inf["n_tiles"] > 0]
+        for i in self.active:
+            sap_plan_upload(self.plans[i])
+        self.delta = torch.empty((hq, max(self.tq, 1)), dtype=torch.float32, device=device)
+
+    @property
+    def useful_pairs_per_head(self) -> int:
+        return sum(inf["useful_pairs_per_head"] for inf in self.infos)
+
+    @property
+    def useful_flop(self) -> float:
+        """Backward FLOP on allowed pairs: 10 D per pair per query head (recompute of
+        Q K^T and dO V^T, then dV, dK, dQ)."""
+        return 10.0 * self.d * self.hq * self.useful_pairs_per_head
+
+    def rowterm(self, o, dout, q_row_stride: int, stream=None):
+        sap_attn_bwd_rowterm(self.plans[0], o, dout, q_row_stride, self.hq, self.d, self.delta, stream)
+
+    def accumulate(self, i: int, q, k, v, lse, dout, q_row_stride: int, kv_row_stride: int, dq, dk, dv,
+                   stream=None):
+        sap_attn_bwd_accumulate(self.plans[i], q, k, v, lse, self.delta, dout, q_row_stride, kv_row_stride,
+                                self.hq, self.hkv, self.d, self.scale, dq, dk, dv, stream)
+
+    def run(self, q, k, v, o, lse, dout, q_row_stride: int, kv_row_stride: int, dq, dk, dv, stream=None):
+        self.rowterm(o, dout, q_row_stride, stream)
+        for i in self.active:
+            self.accumulate(i, q, k, v, lse, dout, q_row_stride, kv_row_stride, dq, dk, dv, stream)
 
     def close(self):
         for p in self.plans:

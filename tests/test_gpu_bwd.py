@@ -186,3 +186,65 @@ def test_training_fwd_bwd_sampled():
     _check("dK train", dk.cpu().numpy(), dk_ref, cols)
     _check("dV train", dv.cpu().numpy(), dv_ref, cols)
     rf.close()
+
+
+def test_zigzag_rank_fwd_bwd_sampled():
+    """The benchmarked configuration: 128K zigzag GQA rank 3, forward over the
+    ring steps with merges, row terms once, backward per non-empty step;
+    sampled dQ rows and dK/dV rows against the oracle's own forward/backward."""
+    _sap()
+    import torch
+    from long_context_sequence_doc_amd.rank import RankBackward, RankForward
+    w = W.zigzag_rank(3)
+    t = tensors("zigzag", True)
+    say("case zigzag_sp8_128k_gqa_rank3 fwd+bwd (ring steps), sampled rows")
+    steps = [s.kv_segs for s in w.steps]
+    rf = RankForward(w.cu, w.q_segs, steps, w.hq, w.hkv, w.d, w.scale)
+    rb = RankBackward(w.cu, w.q_segs, steps, w.hq, w.hkv, w.d, w.scale)
+    assert rb.active == [0, 1, 7]
+    ql, dol = W.local_rows(t.q, w.q_segs), W.local_rows(t.do, w.q_segs)
+    qd, dod, kd, vd = to_dev(ql), to_dev(dol), to_dev(t.k), to_dev(t.v)
+    o, lse = rf.run(qd, kd, vd, qd.stride(0), kd.stride(0))
+    dq = torch.zeros((w.tq, w.hq, w.d), device="cuda")
+    dk = torch.zeros((w.total, w.hkv, w.d), device="cuda")
+    dv = torch.zeros_like(dk)
+    rb.run(qd, kd, vd, o, lse, dod, qd.stride(0), kd.stride(0), dq, dk, dv)
+    torch.cuda.synchronize()
+    gq = w.q_global_rows()
+    cu = w.cu
+    allk = np.arange(w.total)
+    k64, v64 = f64(t.k), f64(t.v)
+    # (a) dQ on sampled rows, all heads: the oracle forward on those rows only
+    rng = np.random.default_rng(5)
+    rows = set(rng.integers(0, w.tq, size=48).tolist())
+    pos = {g: r for r, g in enumerate(gq.tolist())}
+    for s0 in cu[:-1].tolist():
+        for g in (s0, s0 + 1):
+            if g in pos:
+                rows.add(pos[g])
+    rows = np.array(sorted(rows))
+    q64, do64 = f64(ql[rows]), f64(dol[rows])
+    o_r, lse_r = A.forward(q64, k64, v64, gq[rows], allk, cu, w.scale)
+    dq_ref, _, _ = A.backward(q64, k64, v64, do64, o_r, lse_r, gq[rows], allk, cu, w.scale,
+                              cols=np.zeros(0, dtype=np.int64))
+    _check("dQ zigzag", dq.cpu().numpy()[rows], dq_ref)
+    # (b) dK / dV of KV head 0 (query heads 0..3) on keys sampled from every
+    #     non-empty step's chunks: the oracle forward on all rows of those heads
+    grp = w.hq // w.hkv
+    cols = set()
+    for st in [w.steps[i] for i in rb.active]:
+        for a_, b_, _ in st.kv_segs:
+            cols.update(rng.integers(a_, b_, size=6).tolist())
+            cols.update((a_, b_ - 1))
+    for s0 in cu[:-1].tolist():               # document starts (keys seen by the most rows)
+        cols.add(s0)
+    cols = np.array(sorted(cols))
+    qh, doh = f64(ql[:, :grp]), f64(dol[:, :grp])
+    kh, vh = k64[:, :1], v64[:, :1]
+    o_h, lse_h = A.forward(qh, kh, vh, gq, allk, cu, w.scale)
+    _, dk_ref, dv_ref = A.backward(qh, kh, vh, doh, o_h, lse_h, gq, allk, cu, w.scale,
+                                   rows=np.zeros(0, dtype=np.int64), cols=cols)
+    _check("dK zigzag (KV head 0)", dk.cpu().numpy()[:, :1], dk_ref, cols)
+    _check("dV zigzag (KV head 0)", dv.cpu().numpy()[:, :1], dv_ref, cols)
+    rf.close()
+    rb.close()
