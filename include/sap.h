@@ -176,8 +176,10 @@ size_t sap_attn_bwd_workspace(sap_plan_t plan, int32_t hq, int32_t d);
  *   dV += P^T dO;  dS = P o (dO v^T - D);  dQ += scale dS k;  dK += scale dS^T q.
  * o / lse_final are the merged forward results over *all* KV rows, so the
  * sum of per-step calls is the full gradient. dq, dk, dv are ACCUMULATED
- * (+=, fp32); the caller zeroes them once. dQ uses fp32 atomics (summation
- * order not fixed). workspace: device, >= sap_attn_bwd_workspace bytes.
+ * (+=, fp32); the caller zeroes them once. No atomics: dK/dV come from a
+ * KV-major pass and dQ from a Q-major pass, each owning its output rows, so
+ * the result is deterministic. workspace: device, >= sap_attn_bwd_workspace
+ * bytes.
  * Plan tile shape must be 64 x 128 (block_m x block_n).
  */
 sap_status sap_attn_bwd(sap_plan_t plan, const void *q, const void *k, const void *v,

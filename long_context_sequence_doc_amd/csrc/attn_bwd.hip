@@ -7,29 +7,31 @@
 // state, recompute instead of storing the big intermediates). With the
 // final, all-KV LSE and O of each query row:
 //     P = exp(scale q.k - LSE)                  on allowed pairs (else 0)
-//     D_r = dO_r . O_r                          (bwd_preprocess_kernel)
+//     D_r = dO_r . O_r                          (bwd_rowterm_kernel)
 //     dV += P^T dO,   dS = P o (dO V^T - D),   dK += scale dS^T Q,   dQ += scale dS K
 // so per-step calls of a ring sum to the full gradient.
 //
-// attn_bwd_kernel: one workgroup = one 128-key KV tile x one KV head; 4 waves
-// own 32 keys each. It walks the Q tiles (64 rows) that meet its KV tile
-// (transposed tile list) and, for each, the query heads of its GQA group:
-//   * S = Q K^T and dP = dO V^T with the wave's K / V rows held in registers
-//     as B operands: P and dS come out of the 32x32 accumulators with keys
-//     across lanes and queries across registers, which is exactly the
-//     B-operand layout of dV^T += dO^T P and dK^T += Q^T dS. Q^T and dO^T are
-//     staged in LDS transposed, with the 4-row groups of every 16 query rows
-//     ordered (0-3, 8-11, 4-7, 12-15) to match the accumulator's row order.
-//   * dQ needs dS with keys as the contraction: dS goes through LDS once and
-//     dQ^T = K^T dS^T runs against a transposed copy of the K tile (staged
-//     once per workgroup); each wave produces 32 of the 128 head dims. The
-//     partial dQ tile is staged in LDS as [query][dim] so the fp32 atomics
-//     into the caller's dQ are row-contiguous (one cache line per 32 lanes),
-//     and each workgroup starts its walk at a different Q tile so the
-//     workgroups sharing Q tiles do not queue on the same rows.
-//   * dK / dV stay in registers across all Q tiles and heads, and are added
-//     to the caller's buffers at the end (each (KV tile, KV head) belongs to
-//     exactly one workgroup, so no atomics).
+// Two kernels share the work so that no output needs atomics (device-scope
+// atomics from the 8 XCDs cannot stay in their L2s and go out to memory):
+//
+// attn_bwd_kv_kernel -- dK, dV. One workgroup = one 128-key KV tile x one KV
+//   head; 4 waves own 32 keys each and walk the Q tiles (64 rows) that meet
+//   the KV tile (transposed tile list) and the query heads of the GQA group:
+//   S = Q K^T and dP = dO V^T with the wave's K / V rows held in registers as
+//   B operands, so P and dS leave the 32x32 accumulators with keys across
+//   lanes and queries across registers -- exactly the B-operand layout of
+//   dV^T += dO^T P and dK^T += Q^T dS. Q^T and dO^T are staged in LDS
+//   transposed, the 4-row groups of every 16 query rows ordered (0-3, 8-11,
+//   4-7, 12-15) to match the accumulator's row order. dK / dV stay in
+//   registers and are added to the caller's buffers once at the end.
+//
+// attn_bwd_dq_kernel -- dQ. One workgroup = one 64-row Q tile x one query
+//   head; 2 waves own 32 query rows each and walk the KV tiles that meet the
+//   Q tile, in 64-key halves. As in the forward, S^T = K Q^T and
+//   dP^T = V dO^T put one query per lane pair, P^T and dS^T come out in the
+//   B-operand layout of dQ^T += K^T dS^T, with K^T staged key-permuted in
+//   LDS. Each workgroup owns its dQ rows: the result is added once at the
+//   end with plain loads and stores.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -49,7 +51,9 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 
 constexpr int BMB = 64;     // query rows per Q tile
 constexpr int BNB = 128;    // keys per KV tile
-constexpr int NT = 256;
+constexpr int NT = 256;     // threads of the KV kernel
+constexpr int NTQ = 128;    // threads of the dQ kernel
+constexpr int NXCD = 8;
 constexpr float LOG2E = 1.4426950408889634f;
 
 __device__ inline bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -74,10 +78,9 @@ __device__ inline u32x2 gather4(const u32x4 (&r)[4], int j) {
 // ---------------------------------------------------------------------------
 // D_r = sum_d dO[r,h,d] * O[r,h,d] for the rows of the plan's Q tiles.
 // 32 threads per (row, head); D/32 elements each.
-__global__ __launch_bounds__(NT) void bwd_preprocess_kernel(const unsigned short *dout, int64_t q_row_stride,
-                                                            const float *o, float *delta,
-                                                            const int32_t *tiles, int32_t hq, int32_t d,
-                                                            int32_t tq) {
+__global__ __launch_bounds__(NT) void bwd_rowterm_kernel(const unsigned short *dout, int64_t q_row_stride,
+                                                         const float *o, float *delta, const int32_t *tiles,
+                                                         int32_t hq, int32_t d, int32_t tq) {
   const int r0 = tiles[2 * blockIdx.x], n = tiles[2 * blockIdx.x + 1];
   const int pair = blockIdx.y * (NT / 32) + threadIdx.x / 32;   // (row, head) index inside the tile
   const int lane = threadIdx.x & 31;
@@ -110,27 +113,19 @@ struct BwdParams {
 };
 
 template <int D>
-struct BwdSmem {
+struct KvSmem {
   static constexpr int RS = D + 8;            // row-major Q / dO row stride (elements)
   static constexpr int TS = BMB + 8;          // transposed Q / dO row stride
-  static constexpr int KTS = BNB + 8;         // transposed K row stride
-  static constexpr int SS = BNB + 8;          // dS row stride
   static constexpr int Q_ROW = 0;
   static constexpr int DO_ROW = Q_ROW + BMB * RS;
   static constexpr int Q_T = DO_ROW + BMB * RS;
   static constexpr int DO_T = Q_T + D * TS;
-  static constexpr int K_T = DO_T + D * TS;
-  static constexpr int DS = K_T + D * KTS;
-  static constexpr int ELEMS = DS + BMB * SS;  // bf16 elements
-  // the dQ staging tile [64][QS] fp32 (row padded against bank conflicts)
-  // reuses the Q / dO row buffers, which are dead by then
-  static constexpr int QS = D + 4;
-  static_assert(BMB * QS * 4 <= 2 * BMB * RS * 2, "dQ staging does not fit in the Q / dO row buffers");
+  static constexpr int ELEMS = DO_T + D * TS;  // bf16 elements
 };
 
 template <int D>
-__global__ __launch_bounds__(NT) void attn_bwd_kernel(BwdParams p) {
-  using S = BwdSmem<D>;
+__global__ __launch_bounds__(NT) void attn_bwd_kv_kernel(BwdParams p) {
+  using S = KvSmem<D>;
   __shared__ __attribute__((aligned(16))) unsigned short lds[S::ELEMS];
   __shared__ float s_lse2[BMB], s_delta[BMB];
   __shared__ int s_ds[BMB];
@@ -159,26 +154,6 @@ __global__ __launch_bounds__(NT) void attn_bwd_kernel(BwdParams p) {
       vf[t] = as_bf16x8(*reinterpret_cast<const u32x4 *>(vp + 16 * t));
     }
   }
-  // K^T of the whole tile into LDS (B operand of dQ = dS K): K_T[d][key]
-  {
-    constexpr int NKG = BNB / 4;               // 32 groups of 4 keys
-    constexpr int ITEMS = NKG * (D / 8);
-#pragma unroll
-    for (int ps = 0; ps < (ITEMS + NT - 1) / NT; ++ps) {
-      const int idx = ps * NT + tid;
-      if (ITEMS % NT != 0 && idx >= ITEMS) break;
-      const int kgp = idx % NKG, dc = idx / NKG;
-      u32x4 r[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = min(kgp * 4 + i, kt.n - 1);
-        r[i] = *reinterpret_cast<const u32x4 *>(p.k + kv_base + int64_t(row) * p.kv_row_stride + 8 * dc);
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        *reinterpret_cast<u32x2 *>(lds + S::K_T + (8 * dc + j) * S::KTS + 4 * kgp) = gather4(r, j);
-    }
-  }
 
   f32x16 dka[D / 32], dva[D / 32];     // dK^T / dV^T blocks: lane = key, registers = d
 #pragma unroll
@@ -188,15 +163,11 @@ __global__ __launch_bounds__(NT) void attn_bwd_kernel(BwdParams p) {
   }
   const float c = p.c;
 
-  // workgroups of neighbouring KV tiles share Q tiles: start each at a
-  // different partner so their dQ atomics do not queue on the same rows
-  const int rot = int((uint32_t(kt.tile) * 2654435761u) % uint32_t(rg.count));
   for (int it = 0; it < rg.count; ++it) {
-    const int pi = it + rot < rg.count ? it + rot : it + rot - rg.count;
-    const PartnerEntry qt = p.partners[rg.begin + pi];
+    const PartnerEntry qt = p.partners[rg.begin + it];
     for (int hi = 0; hi < p.group; ++hi) {
       const int h = g * p.group + hi;
-      __syncthreads();   // previous iteration done with the Q / dO / dS buffers
+      __syncthreads();   // previous iteration done with the Q / dO buffers
       // ---- stage Q and dO rows: row-major and transposed copies
       {
         constexpr int NQG = BMB / 4;           // 16 groups of 4 query rows
@@ -305,65 +276,6 @@ __global__ __launch_bounds__(NT) void attn_bwd_kernel(BwdParams p) {
             dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, pb[qb][u], dva[db], 0, 0, 0);
             dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, sb[qb][u], dka[db], 0, 0, 0);
           }
-
-      // ---- dS -> LDS as [query][key] (bf16); element i of block qb is row
-      //      qb*32 + 8*(i/4) + 4*hf + (i%4): one base address + constant offsets
-      {
-        unsigned short *dsp = lds + S::DS + (4 * hf) * S::SS + my_key;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const u32x4 sk = __builtin_bit_cast(u32x4, sb[qb][u]);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const int i = 8 * u + j;
-              const unsigned word = sk[j >> 1];
-              dsp[(qb * 32 + 8 * (i >> 2) + (i & 3)) * S::SS] =
-                  static_cast<unsigned short>((j & 1) ? (word >> 16) : (word & 0xffffu));
-            }
-          }
-      }
-      __syncthreads();
-
-      // ---- dQ^T[wave's 32 dims][64 queries] = K^T dS^T (k = 128 keys):
-      //      lane = query, registers = dims, so each lane adds into one dQ row
-      if (wave < D / 32) {
-        f32x16 qacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-        for (int t = 0; t < BNB / 16; ++t) {
-          const bf16x8 ak = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + S::K_T + (wave * 32 + l32) * S::KTS + 16 * t + 8 * hf));
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            const bf16x8 bs = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + S::DS + (qb * 32 + l32) * S::SS + 16 * t + 8 * hf));
-            qacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, bs, qacc[qb], 0, 0, 0);
-          }
-        }
-        // accumulator: row = d wave*32 + 8*(i/4) + 4*hf + (i%4), column = query
-        // qb*32 + l32 -> [query][d] fp32 staging in the (now dead) Q / dO row buffers
-        float *stage = reinterpret_cast<float *>(lds + S::Q_ROW);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int ig = 0; ig < 4; ++ig) {
-            f32x4 v4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v4[e] = qacc[qb][4 * ig + e] * p.scale;
-            *reinterpret_cast<f32x4 *>(stage + (qb * 32 + l32) * S::QS + wave * 32 + 8 * ig + 4 * hf) = v4;
-          }
-      }
-      __syncthreads();
-      // ---- row-contiguous atomics: consecutive threads add consecutive dims of one row
-      {
-        const float *stage = reinterpret_cast<const float *>(lds + S::Q_ROW);
-        float *dq_tile = p.dq + (int64_t(qt.local_start) * p.hq + h) * D;
-        const int64_t row_stride = int64_t(p.hq) * D;
-#pragma unroll 4
-        for (int e = tid; e < BMB * D; e += NT) {
-          const int r = e / D, dd = e % D;
-          if (r < qt.n) unsafeAtomicAdd(dq_tile + r * row_stride + dd, stage[r * S::QS + dd]);
-        }
-      }
     }
   }
 
@@ -388,20 +300,188 @@ __global__ __launch_bounds__(NT) void attn_bwd_kernel(BwdParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+constexpr int HK = 64;      // keys per half of a KV tile in the dQ kernel
+
+template <int D>
+struct DqSmem {
+  static constexpr int RS = D + 8;            // row-major K / V row stride (elements)
+  static constexpr int TS = HK + 8;           // transposed K row stride
+  static constexpr int K_ROW = 0;
+  static constexpr int V_ROW = K_ROW + HK * RS;
+  static constexpr int K_T = V_ROW + HK * RS;
+  static constexpr int ELEMS = K_T + D * TS;
+};
+
+template <int D>
+__global__ __launch_bounds__(NTQ) void attn_bwd_dq_kernel(BwdParams p) {
+  using S = DqSmem<D>;
+  __shared__ __attribute__((aligned(16))) unsigned short lds[S::ELEMS];
+
+  // workgroup -> (Q tile, query head); the heads of one KV head and
+  // consecutive Q tiles of one KV head go to the same XCD (ids are dealt
+  // round-robin over the XCDs), to share K / V in its L2
+  const int b = blockIdx.x;
+  const int xcd = b % NXCD, slot = b / NXCD;
+  const int G = (slot / p.group) * NXCD + xcd;
+  if (G >= p.n_work * p.hkv) return;
+  const int w = G / p.hkv, g = G % p.hkv;
+  const int h = g * p.group + slot % p.group;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const WorkItem qt = p.work[w];
+  const WorkRange rg = p.range[w];
+
+  const int my_row = wave * 32 + l32;             // query row within the Q tile
+  const bool row_ok = my_row < qt.n;
+  const int qrow = qt.local_start + min(my_row, qt.n - 1);
+  const int qg = qt.global_start + my_row;
+  const int dsq = p.ds_q[qrow];
+  const float lse = p.lse[int64_t(h) * p.tq + qrow];
+  // rows past the tile end or with no key at all get P = 0
+  const float lse2 = (row_ok && lse != -INFINITY) ? lse * LOG2E : INFINITY;
+  const float dlt = p.delta[int64_t(h) * p.tq + qrow];
+
+  // this lane's Q and dO fragments: B operands of S^T = K Q^T and dP^T = V dO^T
+  bf16x8 qf[D / 16], of[D / 16];
+  {
+    const int64_t off = int64_t(qrow) * p.q_row_stride + int64_t(h) * D + 8 * hf;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      qf[t] = as_bf16x8(*reinterpret_cast<const u32x4 *>(p.q + off + 16 * t));
+      of[t] = as_bf16x8(*reinterpret_cast<const u32x4 *>(p.dout + off + 16 * t));
+    }
+  }
+  f32x16 qacc[D / 32];                            // dQ^T blocks: lane = query, registers = d
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) qacc[i] = f32x16{};
+  const float c = p.c;
+
+  for (int it = 0; it < rg.count; ++it) {
+    const PartnerEntry kt = p.partners[rg.begin + it];
+    for (int half = 0; half * HK < kt.n; ++half) {
+      const int k0 = half * HK;                   // first key of this half within the tile
+      const int kn = min(HK, kt.n - k0);          // keys in this half
+      __syncthreads();   // previous half done with the K / V buffers
+      // ---- stage K rows, V rows and K^T (key-permuted) for 64 keys
+      {
+        constexpr int NKG = HK / 4;               // 16 groups of 4 keys
+        constexpr int ITEMS = NKG * (D / 8);
+        static_assert(ITEMS % NTQ == 0, "staging assumes whole passes");
+        const int64_t base = int64_t(kt.local_start + k0) * p.kv_row_stride + int64_t(g) * D;
+#pragma unroll
+        for (int ps = 0; ps < ITEMS / NTQ; ++ps) {
+          const int idx = ps * NTQ + tid;
+          const int kgp = idx % NKG, dc = idx / NKG;
+          u32x4 rk[4], rv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = min(kgp * 4 + i, kn - 1);
+            const int64_t off = base + int64_t(row) * p.kv_row_stride + 8 * dc;
+            rk[i] = *reinterpret_cast<const u32x4 *>(p.k + off);
+            rv[i] = *reinterpret_cast<const u32x4 *>(p.v + off);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            *reinterpret_cast<u32x4 *>(lds + S::K_ROW + (kgp * 4 + i) * S::RS + 8 * dc) = rk[i];
+            *reinterpret_cast<u32x4 *>(lds + S::V_ROW + (kgp * 4 + i) * S::RS + 8 * dc) = rv[i];
+          }
+          const int col = ((kgp * 4) & ~15) | perm16((kgp * 4) & 15);
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            *reinterpret_cast<u32x2 *>(lds + S::K_T + (8 * dc + j) * S::TS + col) = gather4(rk, j);
+        }
+      }
+      __syncthreads();
+
+      // ---- S^T = K Q^T, dP^T = V dO^T (64 keys x this wave's 32 queries)
+      f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int off = (kb * 32 + l32) * S::RS + 16 * t + 8 * hf;
+          const bf16x8 ak = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + S::K_ROW + off));
+          const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + S::V_ROW + off));
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[t], sacc[kb], 0, 0, 0);
+          pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[t], pacc[kb], 0, 0, 0);
+        }
+
+      // ---- dS^T = P^T o (dP^T - D); element i of key block kb is key
+      //      k0 + kb*32 + 8*(i/4) + 4*hf + (i%4) of the tile
+      const bool masked = kt.cls != SAP_TILE_FULL || kn < HK || qt.n < BMB;
+      int lo = -(1 << 30), hi = kn - 1;           // allowed half-local key range of this query
+      if (masked) {
+        if (kt.cls != SAP_TILE_FULL) hi = min(hi, qg - (kt.global_start + k0));
+        if (kt.cls == SAP_TILE_PARTIAL) lo = dsq - (kt.global_start + k0);
+      }
+      const int hi_r = hi - 4 * hf, lo_r = lo - 4 * hf;
+      bf16x8 sb[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          float sv[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int i = 8 * u + j;
+            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], c, -lse2));
+            if (masked) {
+              const int kc = kb * 32 + 8 * (i >> 2) + (i & 3);
+              pr = (kc <= hi_r && kc >= lo_r) ? pr : 0.f;
+            }
+            sv[j] = pr * (pacc[kb][i] - dlt);
+          }
+          u32x4 sk;
+          sk.x = pack_bf16(sv[0], sv[1]);
+          sk.y = pack_bf16(sv[2], sv[3]);
+          sk.z = pack_bf16(sv[4], sv[5]);
+          sk.w = pack_bf16(sv[6], sv[7]);
+          sb[kb][u] = as_bf16x8(sk);
+        }
+
+      // ---- dQ^T += K^T dS^T (k = 16 keys per step; the D/32 blocks are independent chains)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(
+                lds + S::K_T + (db * 32 + l32) * S::TS + kb * 32 + 16 * u + 8 * hf));
+            qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb[kb][u], qacc[db], 0, 0, 0);
+          }
+    }
+  }
+
+  // ---- dQ += scale dQ^T for this lane's query row
+  if (!row_ok) return;
+  float *dqp = p.dq + (int64_t(qrow) * p.hq + h) * D + 4 * hf;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int ig = 0; ig < 4; ++ig) {
+      const int off = db * 32 + 8 * ig;
+      f32x4 a = *reinterpret_cast<f32x4 *>(dqp + off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] += p.scale * qacc[db][4 * ig + e];
+      *reinterpret_cast<f32x4 *>(dqp + off) = a;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_bwd_rowterm(const BwdLaunch &a, hipStream_t stream) {
   if (a.n_touched_q > 65535) return hipErrorInvalidValue;
   const int pairs = a.max_q_rows * a.hq;
   const dim3 grid{static_cast<unsigned>(a.n_touched_q), static_cast<unsigned>((pairs + NT / 32 - 1) / (NT / 32))};
-  hipLaunchKernelGGL(bwd_preprocess_kernel, grid, dim3(NT), 0, stream,
+  hipLaunchKernelGGL(bwd_rowterm_kernel, grid, dim3(NT), 0, stream,
                      static_cast<const unsigned short *>(a.dout), a.q_row_stride, a.o, a.delta, a.touched_rows,
                      a.hq, a.d, a.tq);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_bwd(const BwdLaunch &a, hipStream_t stream) {
-  if (a.n_work > INT32_MAX / a.hkv) return hipErrorInvalidValue;
   BwdParams p;
   p.q = static_cast<const unsigned short *>(a.q);
   p.k = static_cast<const unsigned short *>(a.k);
@@ -414,23 +494,46 @@ hipError_t launch_attn_bwd(const BwdLaunch &a, hipStream_t stream) {
   p.dq = a.dq;
   p.dk = a.dk;
   p.dv = a.dv;
-  p.work = a.work;
-  p.range = a.range;
-  p.partners = a.partners;
   p.ds_q = a.ds_q;
   p.hq = a.hq;
   p.hkv = a.hkv;
   p.group = a.hq / a.hkv;
   p.tq = a.tq;
-  p.n_work = a.n_work;
   p.scale = a.scale;
   p.c = a.scale * LOG2E;
-  const dim3 grid{static_cast<unsigned>(a.n_work * a.hkv)};
-  if (a.d == 128)
-    hipLaunchKernelGGL(attn_bwd_kernel<128>, grid, dim3(NT), 0, stream, p);
-  else
-    hipLaunchKernelGGL(attn_bwd_kernel<64>, grid, dim3(NT), 0, stream, p);
-  return hipGetLastError();
+  // dK, dV: KV-major work
+  if (a.n_work > 0) {
+    if (int64_t(a.n_work) * a.hkv > INT32_MAX) return hipErrorInvalidValue;
+    p.work = a.work;
+    p.range = a.range;
+    p.partners = a.partners;
+    p.n_work = a.n_work;
+    const dim3 grid{static_cast<unsigned>(a.n_work * a.hkv)};
+    if (a.d == 128)
+      hipLaunchKernelGGL(attn_bwd_kv_kernel<128>, grid, dim3(NT), 0, stream, p);
+    else
+      hipLaunchKernelGGL(attn_bwd_kv_kernel<64>, grid, dim3(NT), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // dQ: Q-major work
+  if (a.n_q_work > 0) {
+    p.work = a.q_work;
+    p.range = a.q_range;
+    p.partners = a.q_partners;
+    p.n_work = a.n_q_work;
+    const int64_t slots = (int64_t(a.n_q_work) * a.hkv + NXCD - 1) / NXCD;
+    const int64_t blocks = slots * NXCD * p.group;
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    const dim3 grid{static_cast<unsigned>(blocks)};
+    if (a.d == 128)
+      hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, grid, dim3(NTQ), 0, stream, p);
+    else
+      hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, grid, dim3(NTQ), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace sap

@@ -48,16 +48,20 @@ struct BwdLaunch {
   const int32_t *touched_rows;  // Q tiles of the plan: (local_start, n) pairs
   int32_t n_touched_q;
   int32_t max_q_rows;
-  const WorkItem *work;         // KV-major work
+  const WorkItem *work;         // KV-major work (dK, dV)
   const WorkRange *range;
   const PartnerEntry *partners;
-  const int32_t *ds_q;
   int32_t n_work;
+  const WorkItem *q_work;       // Q-major work (dQ)
+  const WorkRange *q_range;
+  const PartnerEntry *q_partners;
+  int32_t n_q_work;
+  const int32_t *ds_q;
 };
 
 // D_r = dO_r . O_r for the rows of the given tiles
 hipError_t launch_bwd_rowterm(const BwdLaunch &a, hipStream_t stream);
-// dq / dk / dv given a.delta
+// dq / dk / dv given a.delta (a KV-major dK/dV kernel, then a Q-major dQ kernel)
 hipError_t launch_attn_bwd(const BwdLaunch &a, hipStream_t stream);
 
 }  // namespace sap

@@ -277,8 +277,12 @@ void fill_bwd(const sap::Plan &P, sap::BwdLaunch *a) {
   a->work = P.dev.kv_work;
   a->range = P.dev.kv_range;
   a->partners = P.dev.kv_partners;
-  a->ds_q = P.dev.ds_q;
   a->n_work = int32_t(P.kv_work.size());
+  a->q_work = P.dev.q_work;
+  a->q_range = P.dev.q_range;
+  a->q_partners = P.dev.q_partners;
+  a->n_q_work = int32_t(P.q_work.size());
+  a->ds_q = P.dev.ds_q;
 }
 
 sap_status rowterm_impl(sap_plan_t plan, const float *o, const void *dout, int64_t q_row_stride, int32_t hq,
