@@ -34,7 +34,9 @@
 //   end with plain loads and stores.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -127,8 +129,9 @@ template <int D>
 __global__ __launch_bounds__(NT) void attn_bwd_kv_kernel(BwdParams p) {
   using S = KvSmem<D>;
   __shared__ __attribute__((aligned(16))) unsigned short lds[S::ELEMS];
-  __shared__ float s_lse2[BMB], s_delta[BMB];
-  __shared__ int s_ds[BMB];
+  __shared__ __attribute__((aligned(16))) float s_lse2[BMB];
+  __shared__ __attribute__((aligned(16))) float s_delta[BMB];
+  __shared__ __attribute__((aligned(16))) int s_ds[BMB];
 
   const int w = blockIdx.x / p.hkv, g = blockIdx.x % p.hkv;
   if (w >= p.n_work) return;
@@ -163,38 +166,54 @@ __global__ __launch_bounds__(NT) void attn_bwd_kv_kernel(BwdParams p) {
   }
   const float c = p.c;
 
-  for (int it = 0; it < rg.count; ++it) {
-    const PartnerEntry qt = p.partners[rg.begin + it];
-    for (int hi = 0; hi < p.group; ++hi) {
-      const int h = g * p.group + hi;
+  // The (Q tile, query head) iterations run in order it * group + hi. The
+  // global loads of the next iteration's Q / dO rows are issued right after
+  // the current ones are staged, so their latency hides behind the math.
+  constexpr int NQG = BMB / 4;                 // 16 groups of 4 query rows
+  constexpr int ITEMS = NQG * (D / 8);
+  constexpr int PASSES = (ITEMS + NT - 1) / NT;
+  const int n_iter = rg.count * p.group;
+  u32x4 rq[PASSES][4], rd[PASSES][4];
+  auto load_rows = [&](int itr) {
+    const PartnerEntry t = p.partners[rg.begin + itr / p.group];
+    const int hh = g * p.group + itr % p.group;
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int idx = ps * NT + tid;
+      const int qgp = idx % NQG, dc = (idx / NQG) % (D / 8);   // in range also for idle passes
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = min(qgp * 4 + i, t.n - 1);
+        const int64_t off = int64_t(t.local_start + row) * p.q_row_stride + int64_t(hh) * D + 8 * dc;
+        rq[ps][i] = *reinterpret_cast<const u32x4 *>(p.q + off);
+        rd[ps][i] = *reinterpret_cast<const u32x4 *>(p.dout + off);
+      }
+    }
+  };
+  load_rows(0);
+
+  for (int itr = 0; itr < n_iter; ++itr) {
+    const PartnerEntry qt = p.partners[rg.begin + itr / p.group];
+    const int h = g * p.group + itr % p.group;
+    {
       __syncthreads();   // previous iteration done with the Q / dO buffers
       // ---- stage Q and dO rows: row-major and transposed copies
       {
-        constexpr int NQG = BMB / 4;           // 16 groups of 4 query rows
-        constexpr int ITEMS = NQG * (D / 8);
 #pragma unroll
-        for (int ps = 0; ps < (ITEMS + NT - 1) / NT; ++ps) {
+        for (int ps = 0; ps < PASSES; ++ps) {
           const int idx = ps * NT + tid;
           if (ITEMS % NT != 0 && idx >= ITEMS) break;
           const int qgp = idx % NQG, dc = idx / NQG;
-          u32x4 rq[4], rd[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int row = min(qgp * 4 + i, qt.n - 1);
-            const int64_t off = int64_t(qt.local_start + row) * p.q_row_stride + int64_t(h) * D + 8 * dc;
-            rq[i] = *reinterpret_cast<const u32x4 *>(p.q + off);
-            rd[i] = *reinterpret_cast<const u32x4 *>(p.dout + off);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<u32x4 *>(lds + S::Q_ROW + (qgp * 4 + i) * S::RS + 8 * dc) = rq[i];
-            *reinterpret_cast<u32x4 *>(lds + S::DO_ROW + (qgp * 4 + i) * S::RS + 8 * dc) = rd[i];
+            *reinterpret_cast<u32x4 *>(lds + S::Q_ROW + (qgp * 4 + i) * S::RS + 8 * dc) = rq[ps][i];
+            *reinterpret_cast<u32x4 *>(lds + S::DO_ROW + (qgp * 4 + i) * S::RS + 8 * dc) = rd[ps][i];
           }
           const int col = ((qgp * 4) & ~15) | perm16((qgp * 4) & 15);
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            *reinterpret_cast<u32x2 *>(lds + S::Q_T + (8 * dc + j) * S::TS + col) = gather4(rq, j);
-            *reinterpret_cast<u32x2 *>(lds + S::DO_T + (8 * dc + j) * S::TS + col) = gather4(rd, j);
+            *reinterpret_cast<u32x2 *>(lds + S::Q_T + (8 * dc + j) * S::TS + col) = gather4(rq[ps], j);
+            *reinterpret_cast<u32x2 *>(lds + S::DO_T + (8 * dc + j) * S::TS + col) = gather4(rd[ps], j);
           }
         }
         if (tid < BMB) {
@@ -204,9 +223,11 @@ __global__ __launch_bounds__(NT) void attn_bwd_kv_kernel(BwdParams p) {
           // rows past the tile end or with no key at all get P = 0
           s_lse2[tid] = (tid < qt.n && l != -INFINITY) ? l * LOG2E : INFINITY;
           s_delta[tid] = p.delta[li];
-          s_ds[tid] = p.ds_q[qt.local_start + row];
+          // document start bounds keys only in PARTIAL tiles
+          s_ds[tid] = qt.cls == SAP_TILE_PARTIAL ? p.ds_q[qt.local_start + row] : INT_MIN;
         }
       }
+      if (itr + 1 < n_iter) load_rows(itr + 1);
       __syncthreads();
 
       // ---- S = Q K^T, dP = dO V^T (64 queries x this wave's 32 keys)
@@ -228,40 +249,64 @@ __global__ __launch_bounds__(NT) void attn_bwd_kv_kernel(BwdParams p) {
         }
 
       // ---- P and dS; accumulator element i of block qb is query row
-      //      qb*32 + 8*(i/4) + 4*hf + (i%4), key my_key
+      //      qb*32 + 8*(i/4) + 4*hf + (i%4), key my_key. The per-row terms of a
+      //      lane's 16 rows come as four 4-row vector reads per block.
       const bool masked = qt.cls != SAP_TILE_FULL || qt.n < BMB || kt.n < BNB;
+      // a row r sees this lane's key iff r >= rmin (causality; invalid keys see
+      // no row) and kg >= s_ds[r] (document start; INT_MIN unless PARTIAL)
+      const int rmin = key_ok ? kg - qt.global_start : (1 << 30);
       bf16x8 pb[2][2], sb[2][2];
+      auto p_and_ds = [&](auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < 2; ++qb) {
+          f32x4 l4[4], d4[4];
+          int ds4[4][4];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          float pv[8], sv[8];
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int r0 = qb * 32 + 8 * g4 + 4 * hf;
+            l4[g4] = *reinterpret_cast<const f32x4 *>(s_lse2 + r0);
+            d4[g4] = *reinterpret_cast<const f32x4 *>(s_delta + r0);
+            if (MASK) {
+              const u32x4 dsv = *reinterpret_cast<const u32x4 *>(s_ds + r0);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int i = 8 * u + j;
-            const int r = qb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][i], c, -s_lse2[r]));
-            if (masked) {
-              const int qg = qt.global_start + r;
-              bool ok = key_ok && kg <= qg;
-              if (qt.cls == SAP_TILE_PARTIAL) ok = ok && kg >= s_ds[r];
-              pr = ok ? pr : 0.f;
+              for (int e = 0; e < 4; ++e) ds4[g4][e] = int(dsv[e]);
             }
-            pv[j] = pr;
-            sv[j] = pr * (pacc[qb][i] - s_delta[r]);
           }
-          u32x4 pk, sk;
-          pk.x = pack_bf16(pv[0], pv[1]);
-          pk.y = pack_bf16(pv[2], pv[3]);
-          pk.z = pack_bf16(pv[4], pv[5]);
-          pk.w = pack_bf16(pv[6], pv[7]);
-          sk.x = pack_bf16(sv[0], sv[1]);
-          sk.y = pack_bf16(sv[2], sv[3]);
-          sk.z = pack_bf16(sv[4], sv[5]);
-          sk.w = pack_bf16(sv[6], sv[7]);
-          pb[qb][u] = as_bf16x8(pk);
-          sb[qb][u] = as_bf16x8(sk);
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            float pv[8], sv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const int i = 8 * u + j;
+              const int g4 = i >> 2, e = i & 3;
+              float x = __builtin_fmaf(sacc[qb][i], c, -l4[g4][e]);
+              if (MASK) {          // masked pairs: exp2(-inf) = 0 (a select, not a branch)
+                const int r = qb * 32 + 8 * g4 + 4 * hf + e;
+                x = ((r >= rmin) & (kg >= ds4[g4][e])) ? x : -INFINITY;
+              }
+              const float pr = __builtin_amdgcn_exp2f(x);
+              pv[j] = pr;
+              sv[j] = pr * (pacc[qb][i] - d4[g4][e]);
+            }
+            u32x4 pk, sk;
+            pk.x = pack_bf16(pv[0], pv[1]);
+            pk.y = pack_bf16(pv[2], pv[3]);
+            pk.z = pack_bf16(pv[4], pv[5]);
+            pk.w = pack_bf16(pv[6], pv[7]);
+            sk.x = pack_bf16(sv[0], sv[1]);
+            sk.y = pack_bf16(sv[2], sv[3]);
+            sk.z = pack_bf16(sv[4], sv[5]);
+            sk.w = pack_bf16(sv[6], sv[7]);
+            pb[qb][u] = as_bf16x8(pk);
+            sb[qb][u] = as_bf16x8(sk);
+          }
         }
+      };
+      if (masked)
+        p_and_ds(std::true_type{});
+      else
+        p_and_ds(std::false_type{});
 
       // ---- dV^T += dO^T P, dK^T += Q^T dS (k = 16 query rows per step)
 #pragma unroll
@@ -425,11 +470,12 @@ __global__ __launch_bounds__(NTQ) void attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int i = 8 * u + j;
-            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], c, -lse2));
-            if (masked) {
+            float x = __builtin_fmaf(sacc[kb][i], c, -lse2);
+            if (masked) {            // masked pairs: exp2(-inf) = 0 (a select, not a branch)
               const int kc = kb * 32 + 8 * (i >> 2) + (i & 3);
-              pr = (kc <= hi_r && kc >= lo_r) ? pr : 0.f;
+              x = (kc <= hi_r && kc >= lo_r) ? x : -INFINITY;
             }
+            const float pr = __builtin_amdgcn_exp2f(x);
             sv[j] = pr * (pacc[kb][i] - dlt);
           }
           u32x4 sk;
