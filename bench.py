@@ -3,13 +3,16 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload zigzag|ring|ulysses|train|tiny]
                     [--forward-only] [--no-cpu-baseline]
 
-A step is one pass of the rank's whole hot path over resident inputs: for
-the default 128K zigzag GQA shard (131072-token packed sequence, SP degree 8,
-rank 3 holds 16384 query rows, 32 query / 8 KV heads, head_dim 128) that is
-the forward of every non-empty ring step with the exact LSE merges, then the
-recompute backward (row terms once, one accumulate call per non-empty step)
-with the final O and LSE. Plans are built once, outside the timed region.
-Prints ONE JSON line.
+A step is one pass of the rank's hot path over resident inputs. For the
+default 128K zigzag GQA shard (131072-token packed sequence, SP degree 8,
+rank 3 holds 16384 query rows, 32 query / 8 KV heads, head_dim 128) the step
+of the headline value is that shard's forward: every non-empty ring step
+with its exact LSE merge. The same shard's training step -- that forward,
+then the recompute backward (row terms once, one accumulate call per
+non-empty step) with the final O and LSE -- is timed after it and reported
+under "training_step" (skip it with --forward-only). For the 64K training
+workload the headline step is forward + backward. Plans are built once,
+outside the timed regions. Prints ONE JSON line.
 
 Throughput counts only allowed (unmasked) query-key pairs: 4 * head_dim FLOP
 per pair per query head for the forward and 10 * head_dim for the backward
@@ -45,7 +48,7 @@ def _args():
     ap.add_argument("--workload", default="zigzag", choices=["zigzag", "ring", "ulysses", "train", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--forward-only", action="store_true",
-                    help="time only the forward ring steps and merges (no backward)")
+                    help="skip the training-step (forward + backward) measurement of forward workloads")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before the run, one plain device-to-device copy of this many MiB (a known-size "
                          "reference for HBM byte counters)")
@@ -152,17 +155,20 @@ def main():
     from long_context_sequence_doc_amd.rank import RankBackward, RankForward
 
     w = W.by_name(a.workload)
-    fwd_only = a.forward_only
-    t = W.make_tensors(w, with_do=not fwd_only)
+    # the training workload's own step is forward + backward; the others' is
+    # the forward with its merges, and their training step is reported beside it
+    headline_bwd = w.backward
+    with_bwd = headline_bwd or not a.forward_only
+    t = W.make_tensors(w, with_do=with_bwd)
     t_plan0 = time.perf_counter()
     kv_steps = [s.kv_segs for s in w.steps]
     rf = RankForward(w.cu, w.q_segs, kv_steps, w.hq, w.hkv, w.d, w.scale)
-    rb = None if fwd_only else RankBackward(w.cu, w.q_segs, kv_steps, w.hq, w.hkv, w.d, w.scale)
+    rb = RankBackward(w.cu, w.q_segs, kv_steps, w.hq, w.hkv, w.d, w.scale) if with_bwd else None
     plan_s = time.perf_counter() - t_plan0
     dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
     q = dev(W.local_rows(t.q, w.q_segs))
     k, v = dev(t.k), dev(t.v)
-    if not fwd_only:
+    if with_bwd:
         dout = dev(W.local_rows(t.do, w.q_segs))
         # gradient buffers are zeroed once; the timed steps keep accumulating into them
         dq = torch.zeros((rf.tq, w.hq, w.d), dtype=torch.float32, device="cuda")
@@ -179,7 +185,7 @@ def main():
 
     qs, ks = q.stride(0), k.stride(0)
 
-    def step(tm):
+    def step(tm, backward):
         for n, i in enumerate(rf.active):
             if n == 0:
                 tm.run("attn_fwd", lambda: sap.sap_attn_fwd(rf.plans[i], q, k, v, qs, ks, w.hq, w.hkv, w.d,
@@ -189,59 +195,63 @@ def main():
                                                             w.scale, rf.o_part, rf.lse_part))
                 tm.run("lse_merge", lambda: sap.sap_lse_merge(rf.plans[i], rf.o, rf.lse, rf.o_part, rf.lse_part,
                                                               rf.tq, w.hq, w.d))
-        if rb is not None:
+        if backward:
             tm.run("bwd_rowterm", lambda: rb.rowterm(rf.o, dout, qs))
             for i in rb.active:
                 tm.run("attn_bwd", lambda: rb.accumulate(i, q, k, v, rf.lse, dout, qs, ks, dq, dk, dv))
 
-    warm = _Timer(stream)
-    for _ in range(a.warmup):
-        step(warm)
-    torch.cuda.synchronize()
-
-    tm = _Timer(stream)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(a.steps):
-        step(tm)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / a.steps
+    def timed(backward):
+        warm = _Timer(stream)
+        for _ in range(a.warmup):
+            step(warm, backward)
+        torch.cuda.synchronize()
+        tm = _Timer(stream)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(a.steps):
+            step(tm, backward)
+        end.record(stream)
+        torch.cuda.synchronize()
+        return tm, start.elapsed_time(end) / a.steps
 
     fwd_flop = rf.useful_flop
-    bwd_flop = 0.0 if rb is None else rb.useful_flop
-    flop = fwd_flop + bwd_flop
-    value = flop / (ms_per_step * 1e-3) / 1e12
+    bwd_flop = rb.useful_flop if rb is not None else 0.0
 
-    def kernel_stats(name, flop_per_step):
+    def kernel_stats(tm, name, flop_per_step):
         n = tm.count(name)
         if not n:
             return None
         ms = tm.ms(name)
-        avg = ms / n
         ach = flop_per_step * a.steps / (ms * 1e-3) / 1e12
-        return {"launches_per_step": n // a.steps, "avg_launch_ms": round(avg, 4), "ms_per_step": round(ms / a.steps, 4),
-                "tflops": round(ach, 3), "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+        return {"launches_per_step": n // a.steps, "avg_launch_ms": round(ms / n, 4),
+                "ms_per_step": round(ms / a.steps, 4), "tflops": round(ach, 3),
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
 
-    fwd = kernel_stats("attn_fwd", fwd_flop)
-    bwd = kernel_stats("attn_bwd", bwd_flop) if rb is not None else None
-    dom_name, dom, dom_flop = ("attn_fwd", fwd, fwd_flop)
-    if bwd is not None and bwd["ms_per_step"] > fwd["ms_per_step"]:
-        dom_name, dom, dom_flop = ("attn_bwd", bwd, bwd_flop)
-    merge_bytes = rf.merge_rows() * (12 * w.d + 12)
-    merge = None
-    if tm.count("lse_merge"):
-        gbs = merge_bytes * a.steps / (tm.ms("lse_merge") * 1e-3) / 1e9
-        merge = {"bound": "hbm", "achieved_gbs": round(gbs, 1), "peak_gbs": PEAK_HBM_GBS,
-                 "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_step": merge_bytes,
-                 "avg_launch_ms": round(tm.ms("lse_merge") / tm.count("lse_merge"), 4)}
-    rowterm = None
-    if tm.count("bwd_rowterm"):
-        # dO (bf16) + O (fp32) read, D written, per (row, head)
-        rt_bytes = rf.tq * w.hq * (6 * w.d + 4)
-        gbs = rt_bytes * a.steps / (tm.ms("bwd_rowterm") * 1e-3) / 1e9
-        rowterm = {"bound": "hbm", "achieved_gbs": round(gbs, 1), "peak_gbs": PEAK_HBM_GBS,
-                   "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_step": rt_bytes}
+    def hbm_stats(tm, name, bytes_per_step):
+        if not tm.count(name):
+            return None
+        gbs = bytes_per_step * a.steps / (tm.ms(name) * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved_gbs": round(gbs, 1), "peak_gbs": PEAK_HBM_GBS,
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_step": bytes_per_step,
+                "avg_launch_ms": round(tm.ms(name) / tm.count(name), 4)}
+
+    merge_bytes = rf.merge_rows() * (12 * w.d + 12)     # O_acc, O_part read, O_acc written; 3 LSE words
+    rowterm_bytes = rf.tq * w.hq * (6 * w.d + 4)         # dO (bf16) and O (fp32) read, D written
+
+    def report(tm, ms_per_step, backward):
+        flop = fwd_flop + (bwd_flop if backward else 0.0)
+        kernels = {"attn_fwd": kernel_stats(tm, "attn_fwd", fwd_flop),
+                   "attn_bwd": kernel_stats(tm, "attn_bwd", bwd_flop) if backward else None,
+                   "lse_merge": hbm_stats(tm, "lse_merge", merge_bytes),
+                   "bwd_rowterm": hbm_stats(tm, "bwd_rowterm", rowterm_bytes) if backward else None}
+        return flop, flop / (ms_per_step * 1e-3) / 1e12, kernels
+
+    tm_h, ms_h = timed(headline_bwd)
+    flop, value, kernels = report(tm_h, ms_h, headline_bwd)
+    dom_name = "attn_fwd"
+    if kernels["attn_bwd"] is not None and kernels["attn_bwd"]["ms_per_step"] > kernels["attn_fwd"]["ms_per_step"]:
+        dom_name = "attn_bwd"
+    dom = kernels[dom_name]
 
     line = {
         "metric": "Effective TFLOP/s (unmasked pairs only) + % of bf16 MFMA peak, 128K packed",
@@ -250,7 +260,7 @@ def main():
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(ms_h, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -259,7 +269,7 @@ def main():
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "config": {
             "workload": w.name,
-            "step": "forward (ring steps + LSE merges)" + ("" if fwd_only else " + recompute backward"),
+            "step": "forward (ring steps + LSE merges)" + (" + recompute backward" if headline_bwd else ""),
             "seq_len": w.total,
             "documents": len(w.lengths),
             "q_rows": w.tq,
@@ -270,7 +280,7 @@ def main():
             "nonempty_steps": len(rf.active),
             "useful_pairs_per_head": rf.useful_pairs_per_head,
             "useful_flop_per_step": flop,
-            "flop_per_pair_per_head": 4 * w.d if fwd_only else 14 * w.d,
+            "flop_per_pair_per_head": (14 if headline_bwd else 4) * w.d,
             "tiles": {"forward": [128, 64], "backward": [64, 128]},
             "plan_host_s": round(plan_s, 3),
         },
@@ -285,10 +295,19 @@ def main():
             "launches_per_step": dom["launches_per_step"],
             "avg_launch_ms": dom["avg_launch_ms"],
         },
-        "kernels": {"attn_fwd": fwd, "attn_bwd": bwd, "lse_merge": merge, "bwd_rowterm": rowterm},
+        "kernels": kernels,
     }
+    if with_bwd and not headline_bwd:
+        # the same shard's training step: forward + merges + recompute backward
+        tm_t, ms_t = timed(True)
+        tflop, tvalue, tkernels = report(tm_t, ms_t, True)
+        line["training_step"] = {"step": "forward (ring steps + LSE merges) + recompute backward",
+                                 "value": round(tvalue, 3), "unit": "TFLOP/s",
+                                 "pct_of_peak": round(100.0 * tvalue / PEAK_BF16_TFLOPS, 2),
+                                 "ms_per_step": round(ms_t, 4), "useful_flop_per_step": tflop,
+                                 "flop_per_pair_per_head": 14 * w.d, "kernels": tkernels}
     if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, t, fwd_only)
+        line["cpu_baseline"] = cpu_baseline(w, t, not headline_bwd)
     rf.close()
     if rb is not None:
         rb.close()
