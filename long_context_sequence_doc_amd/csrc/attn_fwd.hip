@@ -15,19 +15,25 @@
 //     keys), so a query's scores sit in one lane pair (lane, lane ^ 32): row
 //     max/sum are in-register plus a single cross-half exchange.
 //   * P^T (bf16) is already in the B-operand layout of O^T += V^T P^T, so P
-//     never goes through LDS. V^T is the A operand: V is stored transposed
-//     in LDS with the 4-key groups of every 16 keys ordered
-//     (0-3, 8-11, 4-7, 12-15), which is the key order P^T's registers carry;
-//     each operand is then a single 16-byte LDS read.
-//   * K and V^T tiles are double-buffered in LDS: the next tile's global
-//     loads are issued before the current tile's math, stored after it.
+//     never goes through LDS. Its registers carry the keys of every 16-key
+//     step in the order (0-3, 8-11 | 4-7, 12-15) (lane halves), so the V^T
+//     A operand is two ds_read_b64_tr_b16 transposing reads of 4 keys each
+//     from row-major V.
+//   * K and V tiles go from global memory straight into LDS
+//     (global_load_lds_dwordx4: no registers, no VALU) into a double buffer:
+//     the next tile's loads are issued before the current tile's math and
+//     waited for at the barrier that ends it. Each load instruction fills
+//     1 KB of LDS, 16 bytes per lane in lane order, so the layout is chosen
+//     through the global address each lane loads: rows are unpadded and the
+//     16-byte chunks of a row are XOR-swizzled by the row index, which keeps
+//     the matrix-operand reads free of bank conflicts.
 //   * Online softmax in fp32 with exp2 and the scale folded into one FMA.
 //     The running max is only moved (and O, l rescaled) when it grows by
 //     more than 2^8, which keeps the result exact (O / l normalises) while
 //     skipping most rescales.
 //   * Class FULL tiles skip masking; DIAGONAL masks key > query; PARTIAL also
 //     masks keys before the query's document start; ragged tiles mask
-//     columns past the tile end (their K/V rows are zero-filled).
+//     columns past the tile end (their K/V rows repeat the tile's last row).
 //   * Workgroup ids are mapped so that the query heads sharing one KV head
 //     and consecutive work items of one KV head land on the same XCD (ids
 //     are dealt round-robin over the 8 XCDs), to share K/V in that XCD's L2.
@@ -45,15 +51,21 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
 
 constexpr int BM = 128;
 constexpr int BN = 64;
-constexpr int NTHREADS = 256;
+constexpr int NWAVES = 4;
+constexpr int NTHREADS = 64 * NWAVES;
 constexpr int NXCD = 8;
 constexpr float LOG2E = 1.4426950408889634f;
 // running max moves only when the new max exceeds it by more than this many
 // powers of two (p = 2^(s*c - m*c) then stays <= 2^8)
 constexpr float RESCALE_LOG2 = 8.0f;
+static_assert(NWAVES * 32 == BM, "one 32-row slice of the Q tile per wave");
 
 struct FwdParams {
   const unsigned short *q, *k, *v;
@@ -68,107 +80,69 @@ struct FwdParams {
   float scale, c;     // c = scale * log2(e)
 };
 
-__device__ inline int perm16(int key) {
-  // position of a key inside its 16-key group in the V^T LDS layout
-  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
-}
-
+// LDS geometry of one stage: K tile then V tile, each BN rows x D bf16,
+// row-major, unpadded; 16-byte chunk j of row r is stored at chunk position
+// j ^ ksw(r) (K) or j ^ vsw(r) (V).
 template <int D>
-struct Smem {
-  static constexpr int KS = D + 8;        // K row stride (bf16 elements), padded
-  static constexpr int VS = BN + 8;       // V^T row stride
-  static constexpr int KBUF = BN * KS;
-  static constexpr int VBUF = D * VS;
-  static constexpr int BUF = KBUF + VBUF; // one stage
+struct Stage {
+  static constexpr int CPR = D / 8;                    // 16-byte chunks per row
+  static constexpr int ROW = 2 * D;                    // bytes per row
+  static constexpr int TILE = BN * ROW;                // bytes of the K (or V) tile
+  static constexpr int BYTES = 2 * TILE;
+  static constexpr int LOADS = BN * CPR / NTHREADS;    // 16-byte loads per thread per tile
+  static_assert(LOADS * NTHREADS == BN * CPR, "the tile must split evenly over the threads");
+  // K is read as 16-byte row chunks by 32 consecutive rows: chunk ^ (row % CPR)
+  // spreads any run of CPR consecutive rows over distinct chunk positions.
+  static __device__ int ksw(int row) { return row % CPR; }
+  // V is read by ds_read_b64_tr_b16: each 16 lanes take 8 bytes from each of
+  // 4 consecutive rows at 2 adjacent chunks; XOR by 2 * (row % 4) moves the
+  // 4 rows' chunk pairs onto distinct banks.
+  static __device__ int vsw(int row) { return 2 * (row % 4); }
 };
 
-template <int D>
-struct TileRegs {
-  // K: D/32 chunks of 8 elements per thread; V: D/32 keys x 8 d per thread
-  static constexpr int KL = D / 32;
-  static constexpr int VL = D / 32;
-  u32x4 kr[KL];
-  u32x4 vr[VL];
-};
-
-// Per-thread element offsets of the KV tile loads, relative to the tile's
-// first row of the KV head; loop-invariant for full 64-row tiles.
+// Per-thread element offsets (from the tile's first row of the KV head) of
+// the global chunks this thread copies into LDS. Chunk position P of a tile
+// (16 bytes each, in LDS order) is written by load i = P / NTHREADS of wave
+// (P / 64) % NWAVES, lane P % 64. Rows past a short tile's end repeat its last
+// row (finite values; their scores are masked to -inf, their P is 0).
 template <int D>
 struct LoadOffsets {
-  int k[D / 32];
-  int v[D / 32];
+  int k[Stage<D>::LOADS];
+  int v[Stage<D>::LOADS];
 };
 
 template <int D>
-__device__ inline LoadOffsets<D> load_offsets(int stride, int tid, int rows) {
-  constexpr int CPR = D / 8;                 // 16-byte chunks per K row
-  constexpr int RPI = NTHREADS / CPR;        // rows covered per pass
-  constexpr int KPT = D / 32;                // consecutive keys per thread (V)
-  constexpr int NKG = BN / KPT;              // key groups
+__device__ inline LoadOffsets<D> load_offsets(int stride, int wave, int lane, int rows) {
+  using G = Stage<D>;
   LoadOffsets<D> o;
-  const int last = rows - 1;
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) o.k[i] = min(tid / CPR + RPI * i, last) * stride + 8 * (tid % CPR);
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) o.v[i] = min((tid % NKG) * KPT + i, last) * stride + 8 * (tid / NKG);
+  for (int i = 0; i < G::LOADS; ++i) {
+    const int P = (i * NWAVES + wave) * 64 + lane;
+    const int row = P / G::CPR, pos = P % G::CPR;
+    const int src = min(row, rows - 1) * stride;
+    o.k[i] = src + 8 * (pos ^ G::ksw(row));
+    o.v[i] = src + 8 * (pos ^ G::vsw(row));
+  }
   return o;
 }
 
-// Global -> register loads of one KV tile. Rows past a short tile's end are
-// clamped to its last row (finite values; their scores are masked to -inf and
-// their P is 0), so the loads need no per-row branches.
+// Issues the direct global -> LDS copies of one KV tile into a stage.
 template <int D>
-__device__ inline void load_tile(TileRegs<D> &r, const FwdParams &p, const PartnerEntry &pe, int g,
-                                 int tid, const LoadOffsets<D> &full) {
+__device__ inline void issue_tile(const FwdParams &p, const PartnerEntry &pe, int g, unsigned char *stage,
+                                  int wave, int lane, const LoadOffsets<D> &full) {
+  using G = Stage<D>;
   const int64_t base = int64_t(pe.local_start) * p.kv_row_stride + int64_t(g) * D;
   const unsigned short *kb = p.k + base;
   const unsigned short *vb = p.v + base;
-  if (pe.n == BN) {
+  const LoadOffsets<D> o = pe.n == BN ? full : load_offsets<D>(int(p.kv_row_stride), wave, lane, pe.n);
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) r.kr[i] = *reinterpret_cast<const u32x4 *>(kb + full.k[i]);
+  for (int i = 0; i < G::LOADS; ++i)
+    __builtin_amdgcn_global_load_lds((global_void *)(kb + o.k[i]),
+                                     (lds_void *)(stage + (i * NWAVES + wave) * 1024), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) r.vr[i] = *reinterpret_cast<const u32x4 *>(vb + full.v[i]);
-  } else {
-    const LoadOffsets<D> o = load_offsets<D>(int(p.kv_row_stride), tid, pe.n);
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) r.kr[i] = *reinterpret_cast<const u32x4 *>(kb + o.k[i]);
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) r.vr[i] = *reinterpret_cast<const u32x4 *>(vb + o.v[i]);
-  }
-}
-
-template <int D>
-__device__ inline void store_tile(const TileRegs<D> &r, unsigned short *buf, int tid) {
-  using S = Smem<D>;
-  constexpr int CPR = D / 8;
-  constexpr int RPI = NTHREADS / CPR;
-  const int c = tid % CPR;
-#pragma unroll
-  for (int i = 0; i < TileRegs<D>::KL; ++i) {
-    const int row = tid / CPR + RPI * i;
-    *reinterpret_cast<u32x4 *>(buf + row * S::KS + 8 * c) = r.kr[i];
-  }
-  constexpr int KPT = D / 32;
-  constexpr int NKG = BN / KPT;
-  const int kg = tid % NKG, dc = tid / NKG;
-  unsigned short *vt = buf + S::KBUF;
-  const int key0 = kg * KPT;
-  const int col = (key0 & ~15) | perm16(key0 & 15);
-  // transpose: for each of the 8 d values gather the KPT keys' elements
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int w = j >> 1;
-    const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
-    unsigned short *dst = vt + (8 * dc + j) * S::VS + col;
-    if constexpr (KPT == 4) {
-      u32x2 pk;
-      pk.x = __builtin_amdgcn_perm(r.vr[1][w], r.vr[0][w], sel);
-      pk.y = __builtin_amdgcn_perm(r.vr[3][w], r.vr[2][w], sel);
-      *reinterpret_cast<u32x2 *>(dst) = pk;
-    } else {
-      *reinterpret_cast<unsigned *>(dst) = __builtin_amdgcn_perm(r.vr[1][w], r.vr[0][w], sel);
-    }
-  }
+  for (int i = 0; i < G::LOADS; ++i)
+    __builtin_amdgcn_global_load_lds((global_void *)(vb + o.v[i]),
+                                     (lds_void *)(stage + G::TILE + (i * NWAVES + wave) * 1024), 16, 0, 0);
 }
 
 __device__ inline bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -184,8 +158,8 @@ __device__ inline unsigned pack_bf16(float lo, float hi) {
 
 template <int D>
 __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(FwdParams p) {
-  using S = Smem<D>;
-  __shared__ __attribute__((aligned(16))) unsigned short lds[2 * S::BUF];
+  using ST = Stage<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * ST::BYTES];
 
   // workgroup -> (work item, query head), XCD-aware
   const int b = blockIdx.x;
@@ -221,33 +195,51 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(FwdParams p) {
   float l_part = 0.f;         // this lane's share of the softmax denominator
   const float c = p.c;
 
-  TileRegs<D> regs;
-  const LoadOffsets<D> full_offs = load_offsets<D>(int(p.kv_row_stride), tid, BN);
+  const LoadOffsets<D> full_offs = load_offsets<D>(int(p.kv_row_stride), wave, lane, BN);
+
+  // LDS byte offsets (within a stage) of this lane's operand reads.
+  // K (A operand of S^T): row l32 (+32 for the second key block), chunk
+  // 2t + hf of k-step t; (2t + hf) ^ sw = 2t ^ (hf ^ sw), so the offset of
+  // step t is k_off ^ (32 t).
+  const int k_off = l32 * ST::ROW + 16 * (hf ^ ST::ksw(l32));
+  // V^T (A operand of O^T += V^T P^T): within each 16-lane group q (lanes
+  // 16q..16q+15), lane s addresses row 4 * (q / 2) + s / 4 (plus the key
+  // step's base) and columns 16 * (q % 2) + 4 * (s % 4) .. +3 of the D/32
+  // block db; the transposing read hands lane s the 4 keys of column
+  // 16 * (q % 2) + s, which is A-operand row l % 32.
+  int v_off[D / 32];
+  {
+    const int q = lane >> 4, s16 = lane & 15;
+    const int vrow = 4 * (q >> 1) + (s16 >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int col = db * 32 + 16 * (q & 1) + 4 * (s16 & 3);
+      v_off[db] = ST::TILE + vrow * ST::ROW + 16 * ((col >> 3) ^ ST::vsw(vrow)) + 2 * (col & 7);
+    }
+  }
   const PartnerEntry *pes = p.partners + rg.begin;
   PartnerEntry pe = pes[0];
-  load_tile<D>(regs, p, pe, g, tid, full_offs);
-  store_tile<D>(regs, lds, tid);
+  issue_tile<D>(p, pe, g, lds, wave, lane, full_offs);
   __syncthreads();
 
   for (int it = 0; it < rg.count; ++it) {
-    const unsigned short *kbuf = lds + (it & 1) * S::BUF;
-    const unsigned short *vbuf = kbuf + S::KBUF;
+    const unsigned char *cur_stage = lds + (it & 1) * ST::BYTES;
     const PartnerEntry cur = pe;
     const bool more = it + 1 < rg.count;
     if (more) {
       pe = pes[it + 1];
-      load_tile<D>(regs, p, pe, g, tid, full_offs);
+      issue_tile<D>(p, pe, g, lds + ((it + 1) & 1) * ST::BYTES, wave, lane, full_offs);
     }
 
     // S^T for 64 keys x this wave's 32 queries: two independent accumulator
     // chains (key blocks) interleaved so each LDS read is issued ahead of use
     f32x16 s[2] = {f32x16{}, f32x16{}};
     {
-      const unsigned short *kp = kbuf + l32 * S::KS + 8 * hf;
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
-        const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + 16 * t));
-        const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + 32 * S::KS + 16 * t));
+        const unsigned char *kp = cur_stage + (k_off ^ (32 * t));
+        const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const u32x4 *>(kp));
+        const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + 32 * ST::ROW));
         s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[t], s[0], 0, 0, 0);
         s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[t], s[1], 0, 0, 0);
       }
@@ -310,19 +302,22 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(FwdParams p) {
     // O^T += V^T P^T: the D/32 output blocks are independent chains, so the
     // inner loop over them keeps several MFMAs and LDS reads in flight
     {
-      const unsigned short *vp = vbuf + l32 * S::VS + 8 * hf;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(vp + db * 32 * S::VS + kb * 32 + 16 * u));
+            // keys kb*32 + 16u + 4hf + (0..3 | 8..11): rows +0 and +8 of the lane's 4-row group
+            const unsigned char *vp = cur_stage + v_off[db] + (kb * 32 + 16 * u) * ST::ROW;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vp));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vp + 8 * ST::ROW));
+            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][u], oacc[db], 0, 0, 0);
           }
     }
 
-    if (more) store_tile<D>(regs, lds + ((it + 1) & 1) * S::BUF, tid);
+    // the next tile's copies have landed and every wave is done with this one
     __syncthreads();
   }
 
