@@ -167,8 +167,17 @@ sap_status sap_lse_merge(sap_plan_t plan, float *o_acc, float *lse_acc,
                          const float *o_part, const float *lse_part,
                          int32_t tq, int32_t hq, int32_t d, void *hip_stream);
 
-/* Workspace bytes sap_attn_bwd needs (fp32 row terms D_i = dO_i . O_i). */
-size_t sap_attn_bwd_workspace(sap_plan_t plan, int32_t hq, int32_t d);
+/*
+ * sap_attn_bwd_workspace -- device workspace bytes of the backward calls:
+ * fp32 row terms D_r = dO_r . O_r ([hq][Tq], omitted when hq == 0) followed
+ * by the fp32 partial dK / dV sums of the plan's split KV tiles (the planner
+ * splits a KV tile whose partner Q tiles are many into chunks handled by
+ * separate workgroups; their partial sums are added up in a fixed order).
+ * sap_attn_bwd needs sap_attn_bwd_workspace(plan, hq, hkv, d) bytes;
+ * sap_attn_bwd_accumulate needs sap_attn_bwd_workspace(plan, 0, hkv, d),
+ * which is 0 when the plan splits nothing. Returns 0 for invalid arguments.
+ */
+size_t sap_attn_bwd_workspace(sap_plan_t plan, int32_t hq, int32_t hkv, int32_t d);
 
 /*
  * sap_attn_bwd -- recompute-based backward of this call's share:
@@ -177,9 +186,11 @@ size_t sap_attn_bwd_workspace(sap_plan_t plan, int32_t hq, int32_t d);
  * o / lse_final are the merged forward results over *all* KV rows, so the
  * sum of per-step calls is the full gradient. dq, dk, dv are ACCUMULATED
  * (+=, fp32); the caller zeroes them once. No atomics: dK/dV come from a
- * KV-major pass and dQ from a Q-major pass, each owning its output rows, so
- * the result is deterministic. workspace: device, >= sap_attn_bwd_workspace
- * bytes.
+ * KV-major pass and dQ from a Q-major pass, each owning its output rows (a
+ * split KV tile's chunks write workspace slots that one pass adds in a fixed
+ * order), so the result is deterministic. workspace: device, 16-byte
+ * aligned, >= sap_attn_bwd_workspace(plan, hq, hkv, d) bytes; its contents
+ * on entry do not matter. Calls sharing one workspace must not overlap.
  * Plan tile shape must be 64 x 128 (block_m x block_n).
  */
 sap_status sap_attn_bwd(sap_plan_t plan, const void *q, const void *k, const void *v,
@@ -205,13 +216,16 @@ sap_status sap_attn_bwd_rowterm(sap_plan_t plan, const float *o, const void *dou
  * sap_attn_bwd_accumulate -- sap_attn_bwd without the row-term pass: the
  * caller passes delta fp32 [Hq][Tq] from sap_attn_bwd_rowterm (it must hold
  * the rows of this plan's touched Q tiles). Same outputs and accumulation
- * rules as sap_attn_bwd. Plan tile shape 64 x 128.
+ * rules as sap_attn_bwd. workspace: device, 16-byte aligned,
+ * >= sap_attn_bwd_workspace(plan, 0, hkv, d) bytes (may be NULL when that
+ * is 0). Plan tile shape 64 x 128.
  */
 sap_status sap_attn_bwd_accumulate(sap_plan_t plan, const void *q, const void *k, const void *v,
                                    const float *lse_final, const float *delta, const void *dout,
                                    int64_t q_row_stride, int64_t kv_row_stride,
                                    int32_t hq, int32_t hkv, int32_t d, float scale,
-                                   float *dq, float *dk, float *dv, void *hip_stream);
+                                   float *dq, float *dk, float *dv,
+                                   void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char *sap_last_error(void);

@@ -71,12 +71,12 @@ _sigs = {
     "sap_plan_free": ([_P], None),
     "sap_attn_fwd": ([_P, _P, _P, _P, _i64, _i64, _i32, _i32, _i32, _f32, _P, _P, _P], _i32),
     "sap_lse_merge": ([_P, _P, _P, _P, _P, _i32, _i32, _i32, _P], _i32),
-    "sap_attn_bwd_workspace": ([_P, _i32, _i32], _sz),
+    "sap_attn_bwd_workspace": ([_P, _i32, _i32, _i32], _sz),
     "sap_attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _i64, _i64, _i32, _i32, _i32, _f32, _P, _P, _P, _P, _sz, _P],
                      _i32),
     "sap_attn_bwd_rowterm": ([_P, _P, _P, _i64, _i32, _i32, _P, _P], _i32),
-    "sap_attn_bwd_accumulate": ([_P, _P, _P, _P, _P, _P, _P, _i64, _i64, _i32, _i32, _i32, _f32, _P, _P, _P, _P],
-                                _i32),
+    "sap_attn_bwd_accumulate": ([_P, _P, _P, _P, _P, _P, _P, _i64, _i64, _i32, _i32, _i32, _f32, _P, _P, _P, _P,
+                                 _sz, _P], _i32),
     "sap_last_error": ([], ctypes.c_char_p),
     "sap_version": ([], _i32),
 }
@@ -201,8 +201,8 @@ def sap_lse_merge(plan, o_acc, lse_acc, o_part, lse_part, tq: int, hq: int, d: i
                               _ptr(o_part), _ptr(lse_part), tq, hq, d, _stream(stream)))
 
 
-def sap_attn_bwd_workspace(plan: Plan, hq: int, d: int) -> int:
-    return int(_lib.sap_attn_bwd_workspace(plan.handle, hq, d))
+def sap_attn_bwd_workspace(plan: Plan, hq: int, hkv: int, d: int) -> int:
+    return int(_lib.sap_attn_bwd_workspace(plan.handle, hq, hkv, d))
 
 
 def sap_attn_bwd(plan: Plan, q, k, v, o, lse_final, dout, q_row_stride: int, kv_row_stride: int, hq: int,
@@ -218,7 +218,8 @@ def sap_attn_bwd_rowterm(plan: Plan, o, dout, q_row_stride: int, hq: int, d: int
 
 
 def sap_attn_bwd_accumulate(plan: Plan, q, k, v, lse_final, delta, dout, q_row_stride: int, kv_row_stride: int,
-                            hq: int, hkv: int, d: int, scale: float, dq, dk, dv, stream=None):
+                            hq: int, hkv: int, d: int, scale: float, dq, dk, dv, workspace=None,
+                            workspace_bytes: int = 0, stream=None):
     _check(_lib.sap_attn_bwd_accumulate(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(lse_final), _ptr(delta),
                                         _ptr(dout), q_row_stride, kv_row_stride, hq, hkv, d, scale, _ptr(dq),
-                                        _ptr(dk), _ptr(dv), _stream(stream)))
+                                        _ptr(dk), _ptr(dv), _ptr(workspace), workspace_bytes, _stream(stream)))

@@ -14,16 +14,21 @@
 // Two kernels share the work so that no output needs atomics (device-scope
 // atomics from the 8 XCDs cannot stay in their L2s and go out to memory):
 //
-// attn_bwd_kv_kernel -- dK, dV. One workgroup = one 128-key KV tile x one KV
-//   head; 4 waves own 32 keys each and walk the Q tiles (64 rows) that meet
-//   the KV tile (transposed tile list) and the query heads of the GQA group:
+// attn_bwd_kv_kernel -- dK, dV. One workgroup = one chunk of a 128-key KV
+//   tile's partner Q tiles x one KV head; 4 waves own 32 keys each and walk
+//   the chunk's Q tiles (64 rows; transposed tile list) and the query heads
+//   of the GQA group:
 //   S = Q K^T and dP = dO V^T with the wave's K / V rows held in registers as
 //   B operands, so P and dS leave the 32x32 accumulators with keys across
 //   lanes and queries across registers -- exactly the B-operand layout of
 //   dV^T += dO^T P and dK^T += Q^T dS. Q^T and dO^T are staged in LDS
 //   transposed, the 4-row groups of every 16 query rows ordered (0-3, 8-11,
 //   4-7, 12-15) to match the accumulator's row order. dK / dV stay in
-//   registers and are added to the caller's buffers once at the end.
+//   registers and are added to the caller's buffers once at the end. KV
+//   tiles with many partners are split into several chunks by the planner
+//   (so the pass has enough workgroups); their chunks store partial sums in
+//   workspace slots and bwd_kv_reduce_kernel adds the slots up in order, so
+//   the result stays deterministic.
 //
 // attn_bwd_dq_kernel -- dQ. One workgroup = one 64-row Q tile x one query
 //   head; 2 waves own 32 query rows each and walk the KV tiles that meet the
@@ -110,6 +115,9 @@ struct BwdParams {
   const WorkRange *range;
   const PartnerEntry *partners;
   const int32_t *ds_q;
+  const int32_t *slot;     // KV-major chunks: workspace slot (-1: add into dk / dv directly)
+  float *partial;          // [2][n_slots][hkv][BNB][D]: unscaled dK^T, then dV^T partial sums
+  int32_t n_slots;
   int32_t hq, hkv, group, tq, n_work;
   float scale, c;   // c = scale * log2(e)
 };
@@ -324,8 +332,30 @@ __global__ __launch_bounds__(NT) void attn_bwd_kv_kernel(BwdParams p) {
     }
   }
 
-  // ---- dK += scale dK^T, dV += dV^T for this wave's keys
   if (!key_ok) return;
+  const int slot = p.slot[w];
+  if (slot >= 0) {
+    // ---- one chunk of a split KV tile: its partial sums go to the slot
+    const int64_t rows = int64_t(p.n_slots) * p.hkv * BNB;
+    float *pk = p.partial + ((int64_t(slot) * p.hkv + g) * BNB + my_key) * D + 4 * hf;
+    float *pv = pk + rows * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) {
+        const int off = db * 32 + 8 * ig;
+        f32x4 a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = dka[db][4 * ig + e];
+          b[e] = dva[db][4 * ig + e];
+        }
+        *reinterpret_cast<f32x4 *>(pk + off) = a;
+        *reinterpret_cast<f32x4 *>(pv + off) = b;
+      }
+    return;
+  }
+  // ---- dK += scale dK^T, dV += dV^T for this wave's keys
   float *dkp = p.dk + (int64_t(kt.local_start + my_key) * p.hkv + g) * D + 4 * hf;
   float *dvp = p.dv + (int64_t(kt.local_start + my_key) * p.hkv + g) * D + 4 * hf;
 #pragma unroll
@@ -343,6 +373,37 @@ __global__ __launch_bounds__(NT) void attn_bwd_kv_kernel(BwdParams p) {
       *reinterpret_cast<f32x4 *>(dkp + off) = a;
       *reinterpret_cast<f32x4 *>(dvp + off) = b;
     }
+}
+
+// ---------------------------------------------------------------------------
+// dK += scale * sum of a split KV tile's partial dK^T slots, dV += sum of its
+// dV^T slots, the slots added in order (deterministic). One workgroup per
+// (split tile, KV head); each thread handles 4 consecutive d of one key.
+__global__ __launch_bounds__(NT) void bwd_kv_reduce_kernel(const ReduceItem *items, const float *partial,
+                                                           int32_t n_slots, int32_t hkv, int32_t d, float scale,
+                                                           float *dk, float *dv) {
+  const ReduceItem it = items[blockIdx.x / hkv];
+  const int g = blockIdx.x % hkv;
+  const int64_t slot_stride = int64_t(hkv) * BNB * d;            // floats per slot
+  const float *pk = partial + (int64_t(it.slot_begin) * hkv + g) * BNB * d;
+  const float *pv = pk + int64_t(n_slots) * slot_stride;
+  const int quads = it.n * (d / 4);
+  for (int idx = threadIdx.x; idx < quads; idx += NT) {
+    const int key = idx / (d / 4), e4 = 4 * (idx % (d / 4));
+    f32x4 sk = *reinterpret_cast<const f32x4 *>(pk + key * d + e4);
+    f32x4 sv = *reinterpret_cast<const f32x4 *>(pv + key * d + e4);
+    for (int c = 1; c < it.slot_count; ++c) {
+      sk += *reinterpret_cast<const f32x4 *>(pk + c * slot_stride + key * d + e4);
+      sv += *reinterpret_cast<const f32x4 *>(pv + c * slot_stride + key * d + e4);
+    }
+    const int64_t o = (int64_t(it.local_start + key) * hkv + g) * d + e4;
+    f32x4 a = *reinterpret_cast<f32x4 *>(dk + o);
+    f32x4 b = *reinterpret_cast<f32x4 *>(dv + o);
+    a += scale * sk;
+    b += sv;
+    *reinterpret_cast<f32x4 *>(dk + o) = a;
+    *reinterpret_cast<f32x4 *>(dv + o) = b;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -541,6 +602,9 @@ hipError_t launch_attn_bwd(const BwdLaunch &a, hipStream_t stream) {
   p.dk = a.dk;
   p.dv = a.dv;
   p.ds_q = a.ds_q;
+  p.slot = a.kv_slot;
+  p.partial = a.partial;
+  p.n_slots = a.n_slots;
   p.hq = a.hq;
   p.hkv = a.hkv;
   p.group = a.hq / a.hkv;
@@ -559,8 +623,15 @@ hipError_t launch_attn_bwd(const BwdLaunch &a, hipStream_t stream) {
       hipLaunchKernelGGL(attn_bwd_kv_kernel<128>, grid, dim3(NT), 0, stream, p);
     else
       hipLaunchKernelGGL(attn_bwd_kv_kernel<64>, grid, dim3(NT), 0, stream, p);
-    const hipError_t e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.n_reduce > 0) {
+      if (int64_t(a.n_reduce) * a.hkv > INT32_MAX) return hipErrorInvalidValue;
+      hipLaunchKernelGGL(bwd_kv_reduce_kernel, dim3(static_cast<unsigned>(a.n_reduce * a.hkv)), dim3(NT), 0, stream,
+                         a.kv_reduce, a.partial, a.n_slots, a.hkv, a.d, a.scale, a.dk, a.dv);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   // dQ: Q-major work
   if (a.n_q_work > 0) {

@@ -57,6 +57,11 @@ struct BwdLaunch {
   const PartnerEntry *q_partners;
   int32_t n_q_work;
   const int32_t *ds_q;
+  const int32_t *kv_slot;       // per KV-major chunk: workspace slot, -1 = owns its dK / dV rows
+  const ReduceItem *kv_reduce;  // split KV tiles: slots to add up
+  int32_t n_reduce;
+  int32_t n_slots;
+  float *partial;               // [2][n_slots][hkv][128][d] fp32 (dK then dV), or nullptr if n_slots == 0
 };
 
 // D_r = dO_r . O_r for the rows of the given tiles

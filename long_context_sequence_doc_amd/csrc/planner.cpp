@@ -228,7 +228,7 @@ sap_status build_plan(const int32_t *cu_in, int32_t n_docs, const sap_segment *q
       tr_c[size_t(pos)] = P.cls[size_t(t)];
     }
   }
-  P.kv_work.clear(); P.kv_range.clear(); P.kv_partners.clear();
+  P.kv_work.clear(); P.kv_range.clear(); P.kv_partners.clear(); P.kv_slot.clear();
   P.kv_partners.reserve(size_t(n_tiles));
   std::vector<int32_t> kv_touched;
   for (size_t ki = 0; ki < P.kv_tiles.size(); ++ki)
@@ -238,15 +238,47 @@ sap_status build_plan(const int32_t *cu_in, int32_t n_docs, const sap_segment *q
     int32_t ki = kv_touched[size_t(i)];
     return kv_ptr[size_t(ki) + 1] - kv_ptr[size_t(ki)];
   });
+  // Chunks of at most `per` partners: at least ~kTargetChunks chunks over the
+  // plan (times the KV heads = workgroups of the dK / dV pass), none shorter
+  // than kMinChunk partners unless the tile itself is.
+  constexpr int64_t kTargetChunks = 128, kMinChunk = 8;
+  const int64_t per = std::max<int64_t>(kMinChunk, (n_tiles + kTargetChunks - 1) / kTargetChunks);
+  std::vector<WorkItem> cw;
+  std::vector<WorkRange> cr;
+  std::vector<int32_t> cs;
+  P.kv_reduce.clear();
+  P.n_kv_slots = 0;
   for (int32_t oi : order) {
     const int32_t ki = kv_touched[size_t(oi)];
     const TileDesc &kt = P.kv_tiles[size_t(ki)];
-    P.kv_work.push_back(WorkItem{kt.local_start, kt.n, kt.global_start, ki});
-    P.kv_range.push_back(WorkRange{int32_t(P.kv_partners.size()), int32_t(kv_ptr[size_t(ki) + 1] - kv_ptr[size_t(ki)])});
+    const WorkItem item{kt.local_start, kt.n, kt.global_start, ki};
+    const int64_t begin = int64_t(P.kv_partners.size());
+    const int64_t cnt = kv_ptr[size_t(ki) + 1] - kv_ptr[size_t(ki)];
     for (int64_t t = kv_ptr[size_t(ki)]; t < kv_ptr[size_t(ki) + 1]; ++t) {
       const TileDesc &qt = P.q_tiles[size_t(tr_q[size_t(t)])];
       P.kv_partners.push_back(PartnerEntry{qt.local_start, qt.global_start, qt.n, tr_c[size_t(t)]});
     }
+    const int64_t nch = (cnt + per - 1) / per;
+    if (nch == 1) {
+      cw.push_back(item);
+      cr.push_back(WorkRange{int32_t(begin), int32_t(cnt)});
+      cs.push_back(-1);
+      continue;
+    }
+    P.kv_reduce.push_back(ReduceItem{kt.local_start, kt.n, P.n_kv_slots, int32_t(nch)});
+    for (int64_t c = 0; c < nch; ++c) {
+      const int64_t b = begin + c * cnt / nch, e = begin + (c + 1) * cnt / nch;
+      cw.push_back(item);
+      cr.push_back(WorkRange{int32_t(b), int32_t(e - b)});
+      cs.push_back(P.n_kv_slots++);
+    }
+  }
+  // heaviest chunk first
+  std::vector<int32_t> corder = lpt_order(cw.size(), [&](int32_t i) { return int64_t(cr[size_t(i)].count); });
+  for (int32_t i : corder) {
+    P.kv_work.push_back(cw[size_t(i)]);
+    P.kv_range.push_back(cr[size_t(i)]);
+    P.kv_slot.push_back(cs[size_t(i)]);
   }
   return SAP_OK;
 }

@@ -59,7 +59,7 @@ sap_status check_uploaded(sap_plan_t plan) {
 
 extern "C" {
 
-int32_t sap_version(void) { return 100; }
+int32_t sap_version(void) { return 200; }
 
 const char *sap_last_error(void) { return g_last_error.c_str(); }
 
@@ -95,12 +95,15 @@ sap_status sap_plan_upload(sap_plan_t plan, void *hip_stream) {
   if (P.dev.base) return ok();
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   // one allocation; each table 256-byte aligned
-  size_t off[8], total = 0;
-  const void *src[8] = {P.q_work.data(), P.q_range.data(), P.q_partners.data(), P.kv_work.data(),
-                        P.kv_range.data(), P.kv_partners.data(), P.ds_q.data(), P.touched_rows.data()};
-  size_t len[8] = {bytes_of(P.q_work), bytes_of(P.q_range), bytes_of(P.q_partners), bytes_of(P.kv_work),
-                   bytes_of(P.kv_range), bytes_of(P.kv_partners), bytes_of(P.ds_q), bytes_of(P.touched_rows)};
-  for (int i = 0; i < 8; ++i) {
+  constexpr int NT = 10;
+  size_t off[NT], total = 0;
+  const void *src[NT] = {P.q_work.data(), P.q_range.data(), P.q_partners.data(), P.kv_work.data(),
+                         P.kv_range.data(), P.kv_partners.data(), P.ds_q.data(), P.touched_rows.data(),
+                         P.kv_slot.data(), P.kv_reduce.data()};
+  size_t len[NT] = {bytes_of(P.q_work), bytes_of(P.q_range), bytes_of(P.q_partners), bytes_of(P.kv_work),
+                    bytes_of(P.kv_range), bytes_of(P.kv_partners), bytes_of(P.ds_q), bytes_of(P.touched_rows),
+                    bytes_of(P.kv_slot), bytes_of(P.kv_reduce)};
+  for (int i = 0; i < NT; ++i) {
     off[i] = total;
     total += align_up(std::max<size_t>(len[i], 1));
   }
@@ -111,7 +114,7 @@ sap_status sap_plan_upload(sap_plan_t plan, void *hip_stream) {
   e = hipMalloc(&base, total);
   if (e == hipErrorOutOfMemory) return fail(SAP_ERR_NO_MEMORY, "hipMalloc of plan tables failed");
   if (e != hipSuccess) return hip_fail(e, "hipMalloc");
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < NT; ++i) {
     if (!len[i]) continue;
     e = hipMemcpyAsync(static_cast<char *>(base) + off[i], src[i], len[i], hipMemcpyHostToDevice, stream);
     if (e != hipSuccess) {
@@ -135,6 +138,8 @@ sap_status sap_plan_upload(sap_plan_t plan, void *hip_stream) {
   P.dev.kv_partners = reinterpret_cast<const sap::PartnerEntry *>(b + off[5]);
   P.dev.ds_q = reinterpret_cast<const int32_t *>(b + off[6]);
   P.dev.touched_rows = reinterpret_cast<const int32_t *>(b + off[7]);
+  P.dev.kv_slot = reinterpret_cast<const int32_t *>(b + off[8]);
+  P.dev.kv_reduce = reinterpret_cast<const sap::ReduceItem *>(b + off[9]);
   P.dev.device = dev;
   return ok();
 }
@@ -253,10 +258,20 @@ sap_status sap_lse_merge(sap_plan_t plan, float *o_acc, float *lse_acc, const fl
   return ok();
 }
 
-size_t sap_attn_bwd_workspace(sap_plan_t plan, int32_t hq, int32_t d) {
-  (void)d;
-  if (!plan || hq <= 0) return 0;
-  return align_up(size_t(hq) * size_t(std::max(plan->p.tq, 1)) * sizeof(float));
+namespace {
+
+// fp32 partial dK and dV of every workspace slot: [2][slots][hkv][block_n][d]
+size_t partial_bytes(const sap::Plan &P, int32_t hkv, int32_t d) {
+  if (P.n_kv_slots == 0) return 0;
+  return align_up(2 * size_t(P.n_kv_slots) * size_t(hkv) * size_t(P.bn) * size_t(d) * sizeof(float));
+}
+
+}  // namespace
+
+size_t sap_attn_bwd_workspace(sap_plan_t plan, int32_t hq, int32_t hkv, int32_t d) {
+  if (!plan || hq < 0 || hkv <= 0 || d <= 0) return 0;
+  const size_t delta = hq > 0 ? align_up(size_t(hq) * size_t(std::max(plan->p.tq, 1)) * sizeof(float)) : 0;
+  return delta + partial_bytes(plan->p, hkv, d);
 }
 
 namespace {
@@ -278,6 +293,10 @@ void fill_bwd(const sap::Plan &P, sap::BwdLaunch *a) {
   a->range = P.dev.kv_range;
   a->partners = P.dev.kv_partners;
   a->n_work = int32_t(P.kv_work.size());
+  a->kv_slot = P.dev.kv_slot;
+  a->kv_reduce = P.dev.kv_reduce;
+  a->n_reduce = int32_t(P.kv_reduce.size());
+  a->n_slots = P.n_kv_slots;
   a->q_work = P.dev.q_work;
   a->q_range = P.dev.q_range;
   a->q_partners = P.dev.q_partners;
@@ -305,12 +324,16 @@ sap_status rowterm_impl(sap_plan_t plan, const float *o, const void *dout, int64
 sap_status accumulate_impl(sap_plan_t plan, const void *q, const void *k, const void *v, const float *lse_final,
                            const float *delta, const void *dout, int64_t q_row_stride, int64_t kv_row_stride,
                            int32_t hq, int32_t hkv, int32_t d, float scale, float *dq, float *dk, float *dv,
-                           hipStream_t stream) {
+                           float *partial, size_t partial_avail, hipStream_t stream) {
   const sap::Plan &P = plan->p;
   if (!(scale > 0.f) || !(scale < 1e30f)) return fail(SAP_ERR_INVALID_ARG, "scale must be positive and finite");
   if (P.kv_work.empty()) return ok();
   sap_status s = check_uploaded(plan);
   if (s != SAP_OK) return s;
+  const size_t need = partial_bytes(P, hkv, d);
+  if (need > 0 && (!partial || partial_avail < need))
+    return fail(SAP_ERR_INVALID_ARG, "workspace too small (see sap_attn_bwd_workspace)");
+  if (partial && !aligned16(partial)) return fail(SAP_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   if (!q || !k || !v || !lse_final || !delta || !dout || !dq || !dk || !dv) return fail(SAP_ERR_INVALID_ARG, "NULL pointer");
   const void *ptrs[] = {q, k, v, lse_final, delta, dout, dq, dk, dv};
   for (const void *p : ptrs)
@@ -322,6 +345,7 @@ sap_status accumulate_impl(sap_plan_t plan, const void *q, const void *k, const 
   a.q_row_stride = q_row_stride; a.kv_row_stride = kv_row_stride;
   a.hq = hq; a.hkv = hkv; a.d = d; a.scale = scale;
   a.dq = dq; a.dk = dk; a.dv = dv;
+  a.partial = partial;
   fill_bwd(P, &a);
   hipError_t e = sap::launch_attn_bwd(a, stream);
   if (e != hipSuccess) return hip_fail(e, "attn_bwd launch");
@@ -342,11 +366,13 @@ sap_status sap_attn_bwd_rowterm(sap_plan_t plan, const float *o, const void *dou
 sap_status sap_attn_bwd_accumulate(sap_plan_t plan, const void *q, const void *k, const void *v,
                                    const float *lse_final, const float *delta, const void *dout,
                                    int64_t q_row_stride, int64_t kv_row_stride, int32_t hq, int32_t hkv,
-                                   int32_t d, float scale, float *dq, float *dk, float *dv, void *hip_stream) {
+                                   int32_t d, float scale, float *dq, float *dk, float *dv, void *workspace,
+                                   size_t workspace_bytes, void *hip_stream) {
   sap_status s = check_bwd_common(plan, hq, hkv, d);
   if (s != SAP_OK) return s;
   if ((s = accumulate_impl(plan, q, k, v, lse_final, delta, dout, q_row_stride, kv_row_stride, hq, hkv, d, scale,
-                           dq, dk, dv, static_cast<hipStream_t>(hip_stream))) != SAP_OK)
+                           dq, dk, dv, static_cast<float *>(workspace), workspace ? workspace_bytes : 0,
+                           static_cast<hipStream_t>(hip_stream))) != SAP_OK)
     return s;
   return ok();
 }
@@ -361,13 +387,16 @@ sap_status sap_attn_bwd(sap_plan_t plan, const void *q, const void *k, const voi
   if (!(scale > 0.f) || !(scale < 1e30f)) return fail(SAP_ERR_INVALID_ARG, "scale must be positive and finite");
   if (plan->p.kv_work.empty()) return ok();
   if (!workspace) return fail(SAP_ERR_INVALID_ARG, "workspace is NULL");
-  if (workspace_bytes < sap_attn_bwd_workspace(plan, hq, d)) return fail(SAP_ERR_INVALID_ARG, "workspace too small");
+  if (workspace_bytes < sap_attn_bwd_workspace(plan, hq, hkv, d)) return fail(SAP_ERR_INVALID_ARG, "workspace too small");
+  if (!aligned16(workspace)) return fail(SAP_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   if (!o) return fail(SAP_ERR_INVALID_ARG, "NULL pointer");
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   float *delta = static_cast<float *>(workspace);
+  const size_t delta_bytes = sap_attn_bwd_workspace(plan, hq, hkv, d) - sap_attn_bwd_workspace(plan, 0, hkv, d);
+  float *partial = reinterpret_cast<float *>(static_cast<char *>(workspace) + delta_bytes);
   if ((s = rowterm_impl(plan, o, dout, q_row_stride, hq, d, delta, stream)) != SAP_OK) return s;
   if ((s = accumulate_impl(plan, q, k, v, lse_final, delta, dout, q_row_stride, kv_row_stride, hq, hkv, d, scale,
-                           dq, dk, dv, stream)) != SAP_OK)
+                           dq, dk, dv, partial, workspace_bytes - delta_bytes, stream)) != SAP_OK)
     return s;
   return ok();
 }

@@ -41,6 +41,16 @@ struct PartnerEntry {
   int32_t cls;        // SAP_TILE_FULL / DIAGONAL / PARTIAL
 };
 
+// A split backward work item whose chunks left partial dK / dV sums in
+// workspace slots [slot_begin, slot_begin + slot_count) of the KV tile at
+// local rows [local_start, local_start + n).
+struct ReduceItem {
+  int32_t local_start;
+  int32_t n;
+  int32_t slot_begin;
+  int32_t slot_count;
+};
+
 // Device copies of the tables (one allocation, see DeviceTables offsets).
 struct DeviceTables {
   void *base = nullptr;
@@ -48,9 +58,11 @@ struct DeviceTables {
   const WorkItem *q_work = nullptr;      // touched Q tiles, heaviest first
   const WorkRange *q_range = nullptr;
   const PartnerEntry *q_partners = nullptr;
-  const WorkItem *kv_work = nullptr;     // touched KV tiles, heaviest first
+  const WorkItem *kv_work = nullptr;     // chunks of touched KV tiles, heaviest first
   const WorkRange *kv_range = nullptr;
   const PartnerEntry *kv_partners = nullptr;
+  const int32_t *kv_slot = nullptr;      // workspace slot of each chunk, -1 = unsplit
+  const ReduceItem *kv_reduce = nullptr; // split KV tiles
   const int32_t *ds_q = nullptr;         // [tq] document start of each local Q row
   const int32_t *touched_rows = nullptr; // [n_touched] (local_start, n) pairs, ascending
   int device = -1;
@@ -66,10 +78,17 @@ struct Plan {
   std::vector<uint8_t> cls;
   int64_t useful = 0;
   int64_t n_class[3] = {0, 0, 0};
-  // forward work (Q-major) and backward work (KV-major)
+  // forward work (Q-major) and backward work (KV-major). A KV tile with many
+  // partner Q tiles is split into chunks (kv_work / kv_range entries of the
+  // same tile over consecutive partner runs) so the dK / dV pass has enough
+  // workgroups; each chunk of a split tile owns a workspace slot (kv_slot,
+  // -1 for unsplit tiles) that kv_reduce lists per tile.
   std::vector<WorkItem> q_work, kv_work;
   std::vector<WorkRange> q_range, kv_range;
   std::vector<PartnerEntry> q_partners, kv_partners;
+  std::vector<int32_t> kv_slot;
+  std::vector<ReduceItem> kv_reduce;
+  int32_t n_kv_slots = 0;
   std::vector<int32_t> ds_q;
   std::vector<int32_t> touched;       // touched Q tile ids, ascending
   std::vector<int32_t> touched_rows;  // (local_start, n) of touched Q tiles, ascending

@@ -28,7 +28,7 @@ from typing import List, Sequence, Tuple
 
 import torch
 
-from . import (sap_attn_bwd_accumulate, sap_attn_bwd_rowterm, sap_attn_fwd, sap_lse_merge, sap_plan,
+from . import (sap_attn_bwd_accumulate, sap_attn_bwd_rowterm, sap_attn_bwd_workspace, sap_attn_fwd, sap_lse_merge, sap_plan,
                sap_plan_free, sap_plan_info, sap_plan_q_tiles, sap_plan_upload)
 
 BLOCK_M, BLOCK_N = 128, 64
@@ -101,7 +101,9 @@ class RankBackward:
         touches every local row): D_r = dO_r . O_r;
         sap_attn_bwd_accumulate per non-empty ring step, adding that step's
         share into the caller's dq / dk / dv (zeroed by the caller once per
-        training step); the shares sum to the full gradient."""
+        training step); the shares sum to the full gradient. The steps run in
+        order on one stream and share one workspace (partial sums of split
+        KV tiles)."""
 
     BLOCK_M, BLOCK_N = 64, 128
 
@@ -119,6 +121,8 @@ class RankBackward:
         for i in self.active:
             sap_plan_upload(self.plans[i])
         self.delta = torch.empty((hq, max(self.tq, 1)), dtype=torch.float32, device=device)
+        self.ws_bytes = max([sap_attn_bwd_workspace(self.plans[i], 0, hkv, d) for i in self.active] + [0])
+        self.ws = torch.empty(max(self.ws_bytes // 4, 4), dtype=torch.float32, device=device)
 
     @property
     def useful_pairs_per_head(self) -> int:
@@ -136,7 +140,7 @@ class RankBackward:
     def accumulate(self, i: int, q, k, v, lse, dout, q_row_stride: int, kv_row_stride: int, dq, dk, dv,
                    stream=None):
         sap_attn_bwd_accumulate(self.plans[i], q, k, v, lse, self.delta, dout, q_row_stride, kv_row_stride,
-                                self.hq, self.hkv, self.d, self.scale, dq, dk, dv, stream)
+                                self.hq, self.hkv, self.d, self.scale, dq, dk, dv, self.ws, self.ws_bytes, stream)
 
     def run(self, q, k, v, o, lse, dout, q_row_stride: int, kv_row_stride: int, dq, dk, dv, stream=None):
         self.rowterm(o, dout, q_row_stride, stream)

@@ -89,4 +89,27 @@ def test_empty_calls_launch_nothing():
 
 def test_workspace_size():
     p = _plan(bm=64, bn=128)
-    assert sap.sap_attn_bwd_workspace(p, 5, 128) >= 5 * 100 * 4
+    assert sap.sap_attn_bwd_workspace(p, 5, 5, 128) >= 5 * 100 * 4
+    assert sap.sap_attn_bwd_workspace(p, 5, 0, 128) == 0          # invalid hkv
+    assert sap.sap_attn_bwd_workspace(p, -1, 5, 128) == 0
+
+
+def test_bwd_split_workspace():
+    """A KV tile met by many Q tiles is split into chunks whose partial dK / dV
+    sums need workspace (2 x slots x hkv x 128 x d fp32); a short causal
+    document splits nothing."""
+    small = sap.sap_plan([0, 300], [(0, 300, 0)], [(0, 300, 0)], 64, 128)
+    assert sap.sap_attn_bwd_workspace(small, 0, 2, 64) == 0
+    assert sap.sap_attn_bwd_workspace(small, 2, 2, 64) == sap.sap_attn_bwd_workspace(small, 2, 1, 64) > 0
+    # one 8192-token document, Q = its second half against KV = its first
+    # half: every one of the 32 KV tiles meets all 64 Q tiles
+    big = sap.sap_plan([0, 8192], [(4096, 8192, 0)], [(0, 4096, 0)], 64, 128)
+    info = sap.sap_plan_info(big)
+    assert info["n_tiles"] == 32 * 64
+    ws = sap.sap_attn_bwd_workspace(big, 0, 2, 64)
+    per_slot = 2 * 2 * 128 * 64 * 4
+    assert ws > 0 and ws % 256 == 0
+    slots = ws // per_slot
+    # chunks of max(8, ceil(2048 / 128)) = 16 partners: 4 per KV tile
+    assert slots == 32 * 4
+    assert sap.sap_attn_bwd_workspace(big, 3, 2, 64) >= ws + 3 * 4096 * 4

@@ -46,7 +46,7 @@ def _bwd_call(sap, cu, q_segs, kv_segs, qd, kd, vd, dod, o, lse, hq, hkv, d, sca
     info = sap.sap_plan_info(plan)
     if info["n_tiles"]:
         sap.sap_plan_upload(plan)
-    ws_bytes = sap.sap_attn_bwd_workspace(plan, hq, d)
+    ws_bytes = sap.sap_attn_bwd_workspace(plan, hq, hkv, d)
     ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")
     sap.sap_attn_bwd(plan, qd, kd, vd, o, lse, dod, qd.stride(0), kd.stride(0), hq, hkv, d, scale,
                      dq, dk, dv, ws, ws.numel() * 4)
