@@ -162,7 +162,8 @@ def main():
     t = W.make_tensors(w, with_do=with_bwd)
     t_plan0 = time.perf_counter()
     kv_steps = [s.kv_segs for s in w.steps]
-    rf = RankForward(w.cu, w.q_segs, kv_steps, w.hq, w.hkv, w.d, w.scale)
+    # partial buffers are kept for the two-pass (separate merge kernel) reference line
+    rf = RankForward(w.cu, w.q_segs, kv_steps, w.hq, w.hkv, w.d, w.scale, fused_merge=False)
     rb = RankBackward(w.cu, w.q_segs, kv_steps, w.hq, w.hkv, w.d, w.scale) if with_bwd else None
     plan_s = time.perf_counter() - t_plan0
     dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
@@ -185,11 +186,15 @@ def main():
 
     qs, ks = q.stride(0), k.stride(0)
 
-    def step(tm, backward):
+    def step(tm, backward, fused=True):
         for n, i in enumerate(rf.active):
             if n == 0:
                 tm.run("attn_fwd", lambda: sap.sap_attn_fwd(rf.plans[i], q, k, v, qs, ks, w.hq, w.hkv, w.d,
                                                             w.scale, rf.o, rf.lse))
+            elif fused:
+                # this step's partial merged into the running O / LSE in the kernel epilogue
+                tm.run("attn_fwd", lambda: sap.sap_attn_fwd_merge(rf.plans[i], q, k, v, qs, ks, w.hq, w.hkv, w.d,
+                                                                  w.scale, rf.o, rf.lse))
             else:
                 tm.run("attn_fwd", lambda: sap.sap_attn_fwd(rf.plans[i], q, k, v, qs, ks, w.hq, w.hkv, w.d,
                                                             w.scale, rf.o_part, rf.lse_part))
@@ -200,16 +205,16 @@ def main():
             for i in rb.active:
                 tm.run("attn_bwd", lambda: rb.accumulate(i, q, k, v, rf.lse, dout, qs, ks, dq, dk, dv))
 
-    def timed(backward):
+    def timed(backward, fused=True):
         warm = _Timer(stream)
         for _ in range(a.warmup):
-            step(warm, backward)
+            step(warm, backward, fused)
         torch.cuda.synchronize()
         tm = _Timer(stream)
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record(stream)
         for _ in range(a.steps):
-            step(tm, backward)
+            step(tm, backward, fused)
         end.record(stream)
         torch.cuda.synchronize()
         return tm, start.elapsed_time(end) / a.steps
@@ -269,7 +274,8 @@ def main():
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "config": {
             "workload": w.name,
-            "step": "forward (ring steps + LSE merges)" + (" + recompute backward" if headline_bwd else ""),
+            "step": ("forward (ring steps, LSE merge in the kernel epilogue)" + (" + recompute backward" if headline_bwd
+                                                                                 else "")),
             "seq_len": w.total,
             "documents": len(w.lengths),
             "q_rows": w.tq,
@@ -297,11 +303,18 @@ def main():
         },
         "kernels": kernels,
     }
+    if len(rf.active) > 1 and not headline_bwd:
+        # reference: the same forward with a separate merge pass per step
+        tm_2, ms_2 = timed(False, fused=False)
+        _, value_2, kernels_2 = report(tm_2, ms_2, False)
+        line["forward_two_pass"] = {"step": "forward (ring steps + separate lse_merge pass per step)",
+                                    "value": round(value_2, 3), "unit": "TFLOP/s", "ms_per_step": round(ms_2, 4),
+                                    "kernels": kernels_2}
     if with_bwd and not headline_bwd:
-        # the same shard's training step: forward + merges + recompute backward
+        # the same shard's training step: forward + recompute backward
         tm_t, ms_t = timed(True)
         tflop, tvalue, tkernels = report(tm_t, ms_t, True)
-        line["training_step"] = {"step": "forward (ring steps + LSE merges) + recompute backward",
+        line["training_step"] = {"step": "forward (ring steps, fused merges) + recompute backward",
                                  "value": round(tvalue, 3), "unit": "TFLOP/s",
                                  "pct_of_peak": round(100.0 * tvalue / PEAK_BF16_TFLOPS, 2),
                                  "ms_per_step": round(ms_t, 4), "useful_flop_per_step": tflop,

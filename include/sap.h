@@ -154,6 +154,23 @@ sap_status sap_attn_fwd(sap_plan_t plan, const void *q, const void *k, const voi
                         float *o, float *lse, void *hip_stream);
 
 /*
+ * sap_attn_fwd_merge -- sap_attn_fwd with the ring step's merge folded into
+ * the kernel epilogue: this call's partial (O_b, L_b) over the plan's KV rows
+ * is merged into the running result o_acc [Tq][Hq][D] / lse_acc [Hq][Tq]
+ * (fp32 device, in place) exactly as sap_lse_merge does,
+ *   L = ln(e^La + e^Lb);  O = e^(La-L) O_a + e^(Lb-L) O_b,
+ * for the rows of touched Q tiles that have at least one allowed key in this
+ * call; every other row keeps its running values. Same tile shape (128 x 64),
+ * arguments and checks as sap_attn_fwd. A ring rank calls sap_attn_fwd for
+ * its first step and sap_attn_fwd_merge for each later step: no partial
+ * buffers, no separate merge pass. Deterministic (no atomics).
+ */
+sap_status sap_attn_fwd_merge(sap_plan_t plan, const void *q, const void *k, const void *v,
+                              int64_t q_row_stride, int64_t kv_row_stride,
+                              int32_t hq, int32_t hkv, int32_t d, float scale,
+                              float *o_acc, float *lse_acc, void *hip_stream);
+
+/*
  * sap_lse_merge -- exact merge of a partial result into a running one:
  *   L = ln(e^La + e^Lb);  O = e^(La-L) O_a + e^(Lb-L) O_b
  * (a side with L = -inf contributes nothing; both -inf leaves O = 0,

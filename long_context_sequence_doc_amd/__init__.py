@@ -19,7 +19,7 @@ import numpy as np
 __all__ = [
     "SapError", "Segment", "PlanStats", "Plan",
     "sap_plan", "sap_plan_upload", "sap_plan_info", "sap_plan_tiles", "sap_plan_q_tiles",
-    "sap_plan_free", "sap_attn_fwd", "sap_lse_merge", "sap_attn_bwd_workspace", "sap_attn_bwd",
+    "sap_plan_free", "sap_attn_fwd", "sap_attn_fwd_merge", "sap_lse_merge", "sap_attn_bwd_workspace", "sap_attn_bwd",
     "sap_attn_bwd_rowterm", "sap_attn_bwd_accumulate",
     "sap_last_error", "sap_version", "lib_path", "SAP_TILE_FULL", "SAP_TILE_DIAGONAL",
     "SAP_TILE_PARTIAL",
@@ -70,6 +70,7 @@ _sigs = {
     "sap_plan_q_tiles": ([_P, _P, _i32, _P, _i32], _i32),
     "sap_plan_free": ([_P], None),
     "sap_attn_fwd": ([_P, _P, _P, _P, _i64, _i64, _i32, _i32, _i32, _f32, _P, _P, _P], _i32),
+    "sap_attn_fwd_merge": ([_P, _P, _P, _P, _i64, _i64, _i32, _i32, _i32, _f32, _P, _P, _P], _i32),
     "sap_lse_merge": ([_P, _P, _P, _P, _P, _i32, _i32, _i32, _P], _i32),
     "sap_attn_bwd_workspace": ([_P, _i32, _i32, _i32], _sz),
     "sap_attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _i64, _i64, _i32, _i32, _i32, _f32, _P, _P, _P, _P, _sz, _P],
@@ -194,6 +195,12 @@ def sap_attn_fwd(plan: Plan, q, k, v, q_row_stride: int, kv_row_stride: int, hq:
                  scale: float, o, lse, stream=None):
     _check(_lib.sap_attn_fwd(plan.handle, _ptr(q), _ptr(k), _ptr(v), q_row_stride, kv_row_stride, hq, hkv, d,
                              scale, _ptr(o), _ptr(lse), _stream(stream)))
+
+
+def sap_attn_fwd_merge(plan: Plan, q, k, v, q_row_stride: int, kv_row_stride: int, hq: int, hkv: int, d: int,
+                       scale: float, o_acc, lse_acc, stream=None):
+    _check(_lib.sap_attn_fwd_merge(plan.handle, _ptr(q), _ptr(k), _ptr(v), q_row_stride, kv_row_stride, hq, hkv, d,
+                                   scale, _ptr(o_acc), _ptr(lse_acc), _stream(stream)))
 
 
 def sap_lse_merge(plan, o_acc, lse_acc, o_part, lse_part, tq: int, hq: int, d: int, stream=None):

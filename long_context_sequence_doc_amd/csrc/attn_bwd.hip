@@ -55,6 +55,10 @@ typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
 
 constexpr int BMB = 64;     // query rows per Q tile
 constexpr int BNB = 128;    // keys per KV tile
@@ -122,24 +126,41 @@ struct BwdParams {
   float scale, c;   // c = scale * log2(e)
 };
 
+// LDS tile of BMB rows x D bf16, row-major and unpadded, filled by direct
+// global -> LDS copies (16 bytes per lane, lane order). Chunk j (16 bytes)
+// of row r sits at chunk position j ^ sw(r), sw(r) = 2 (r % 4) + (r / 4) % 2
+// (+ 8 ((r / 8) % 2) when a row has 16 chunks): any 8 consecutive rows put
+// one chunk on 8 distinct bank groups (row-operand reads, ds_read_b128), and
+// any 4 rows r0..r0+3 (r0 % 4 == 0) put a chunk pair {2m, 2m+1} on 8
+// distinct positions (transposing reads, ds_read_b64_tr_b16).
 template <int D>
-struct KvSmem {
-  static constexpr int RS = D + 8;            // row-major Q / dO row stride (elements)
-  static constexpr int TS = BMB + 8;          // transposed Q / dO row stride
-  static constexpr int Q_ROW = 0;
-  static constexpr int DO_ROW = Q_ROW + BMB * RS;
-  static constexpr int Q_T = DO_ROW + BMB * RS;
-  static constexpr int DO_T = Q_T + D * TS;
-  static constexpr int ELEMS = DO_T + D * TS;  // bf16 elements
+struct RowTile {
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  static constexpr int ROW = 2 * D;                  // bytes per row
+  static constexpr int BYTES = BMB * ROW;
+  static __device__ int sw(int r) {
+    const int s = 2 * (r & 3) + ((r >> 2) & 1);
+    return CPR >= 16 ? s + 8 * ((r >> 3) & 1) : s;
+  }
+};
+
+template <int D>
+struct KvStage {
+  static constexpr int Q = 0;                        // Q rows of the (Q tile, head)
+  static constexpr int DO = RowTile<D>::BYTES;       // dO rows
+  static constexpr int LSE2 = 2 * RowTile<D>::BYTES; // float[BMB]: LSE * log2(e) (+inf: row sees no key)
+  static constexpr int DELTA = LSE2 + 4 * BMB;       // float[BMB]
+  static constexpr int DS = DELTA + 4 * BMB;         // int[BMB]: document start (INT_MIN unless PARTIAL)
+  static constexpr int BYTES = DS + 4 * BMB;
+  static_assert(BYTES % 1024 == 0 || true, "");
 };
 
 template <int D>
 __global__ __launch_bounds__(NT) void attn_bwd_kv_kernel(BwdParams p) {
-  using S = KvSmem<D>;
-  __shared__ __attribute__((aligned(16))) unsigned short lds[S::ELEMS];
-  __shared__ __attribute__((aligned(16))) float s_lse2[BMB];
-  __shared__ __attribute__((aligned(16))) float s_delta[BMB];
-  __shared__ __attribute__((aligned(16))) int s_ds[BMB];
+  using RT = RowTile<D>;
+  using KS = KvStage<D>;
+  constexpr int STAGE = (KS::BYTES + 1023) & ~1023;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * STAGE];
 
   const int w = blockIdx.x / p.hkv, g = blockIdx.x % p.hkv;
   if (w >= p.n_work) return;
@@ -174,162 +195,229 @@ __global__ __launch_bounds__(NT) void attn_bwd_kv_kernel(BwdParams p) {
   }
   const float c = p.c;
 
-  // The (Q tile, query head) iterations run in order it * group + hi. The
-  // global loads of the next iteration's Q / dO rows are issued right after
-  // the current ones are staged, so their latency hides behind the math.
-  constexpr int NQG = BMB / 4;                 // 16 groups of 4 query rows
-  constexpr int ITEMS = NQG * (D / 8);
-  constexpr int PASSES = (ITEMS + NT - 1) / NT;
+  // Copy geometry: chunk position P = (i * 4 + wave) * 64 + lane of a tile
+  // (i < LOADS) holds row P / CPR, chunk (P % CPR) ^ sw(row).
+  constexpr int LOADS = BMB * RT::CPR / NT;
+  int src_row[LOADS], src_col[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int P = (i * 4 + wave) * 64 + lane;
+    src_row[i] = P / RT::CPR;
+    src_col[i] = 8 * ((P % RT::CPR) ^ RT::sw(P / RT::CPR));
+  }
+  // Row-operand reads (A of S = Q K^T, dP = dO V^T): row qb*32 + l32, chunk
+  // 2t + hf; the offset of step t is r_off ^ (32 t).
+  const int r_off = l32 * RT::ROW + 16 * (hf ^ RT::sw(l32));
+  // Transposing reads (A of dV^T += dO^T P, dK^T += Q^T dS): within each
+  // 16-lane group q, lane s addresses row 4 (q / 2) + s / 4 (+ the step's
+  // base, a multiple of 8) and columns 16 (q % 2) + 4 (s % 4) .. +3 of the
+  // 32-column block db; it receives the 4 rows of column 16 (q % 2) + s.
+  // The +8-row read of a pair flips chunk bit 3 of the swizzle (rows of 16
+  // chunks only).
+  int t_off[D / 32];
+  {
+    const int q4 = lane >> 4, s16 = lane & 15;
+    const int row = 4 * (q4 >> 1) + (s16 >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int col = db * 32 + 16 * (q4 & 1) + 4 * (s16 & 3);
+      t_off[db] = row * RT::ROW + 16 * ((col >> 3) ^ RT::sw(row)) + 2 * (col & 7);
+    }
+  }
+  constexpr int T8 = RT::CPR >= 16 ? 8 * RT::ROW + 0 : 8 * RT::ROW;   // byte distance of the +8-row read
+  auto tr_pair = [&](const unsigned char *tile, int base_row, int db) {
+    const unsigned char *a = tile + t_off[db] + base_row * RT::ROW;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a));
+    const unsigned char *b2 = RT::CPR >= 16 ? tile + ((t_off[db] ^ 128) + base_row * RT::ROW + T8)
+                                            : a + T8;
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(b2));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  // The (Q tile, query head) iterations run in order it * group + hi.
   const int n_iter = rg.count * p.group;
-  u32x4 rq[PASSES][4], rd[PASSES][4];
-  auto load_rows = [&](int itr) {
+  auto issue_rows = [&](int itr, unsigned char *stage) {
     const PartnerEntry t = p.partners[rg.begin + itr / p.group];
     const int hh = g * p.group + itr % p.group;
+    const int64_t base = int64_t(t.local_start) * p.q_row_stride + int64_t(hh) * D;
 #pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-      const int idx = ps * NT + tid;
-      const int qgp = idx % NQG, dc = (idx / NQG) % (D / 8);   // in range also for idle passes
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = min(qgp * 4 + i, t.n - 1);
-        const int64_t off = int64_t(t.local_start + row) * p.q_row_stride + int64_t(hh) * D + 8 * dc;
-        rq[ps][i] = *reinterpret_cast<const u32x4 *>(p.q + off);
-        rd[ps][i] = *reinterpret_cast<const u32x4 *>(p.dout + off);
-      }
+    for (int i = 0; i < LOADS; ++i) {
+      const int64_t off = base + int64_t(min(src_row[i], t.n - 1)) * p.q_row_stride + src_col[i];
+      lds_void *dq = (lds_void *)(stage + KS::Q + (i * 4 + wave) * 1024);
+      lds_void *dd = (lds_void *)(stage + KS::DO + (i * 4 + wave) * 1024);
+      __builtin_amdgcn_global_load_lds((global_void *)(p.q + off), dq, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_void *)(p.dout + off), dd, 16, 0, 0);
     }
   };
-  load_rows(0);
+  // per-row terms of one iteration (threads 0..BMB-1, one row each)
+  float rt_l = 0.f, rt_d = 0.f;
+  int rt_s = 0;
+  auto load_terms = [&](int itr) {
+    const PartnerEntry t = p.partners[rg.begin + itr / p.group];
+    const int hh = g * p.group + itr % p.group;
+    const int row = min(tid, t.n - 1);
+    const int64_t li = int64_t(hh) * p.tq + t.local_start + row;
+    const float l = p.lse[li];
+    // rows past the tile end or with no key at all get P = 0
+    rt_l = (tid < t.n && l != -INFINITY) ? l * LOG2E : INFINITY;
+    rt_d = p.delta[li];
+    // document start bounds keys only in PARTIAL tiles
+    rt_s = t.cls == SAP_TILE_PARTIAL ? p.ds_q[t.local_start + row] : INT_MIN;
+  };
+  auto store_terms = [&](unsigned char *stage) {
+    reinterpret_cast<float *>(stage + KS::LSE2)[tid] = rt_l;
+    reinterpret_cast<float *>(stage + KS::DELTA)[tid] = rt_d;
+    reinterpret_cast<int *>(stage + KS::DS)[tid] = rt_s;
+  };
+
+  issue_rows(0, lds);
+  if (tid < BMB) {
+    load_terms(0);
+    store_terms(lds);
+  }
+  __syncthreads();
 
   for (int itr = 0; itr < n_iter; ++itr) {
     const PartnerEntry qt = p.partners[rg.begin + itr / p.group];
-    const int h = g * p.group + itr % p.group;
-    {
-      __syncthreads();   // previous iteration done with the Q / dO buffers
-      // ---- stage Q and dO rows: row-major and transposed copies
-      {
+    unsigned char *cur = lds + (itr & 1) * STAGE;
+    unsigned char *nxt = lds + ((itr + 1) & 1) * STAGE;
+    const bool more = itr + 1 < n_iter;
+    if (more) {
+      issue_rows(itr + 1, nxt);
+      if (tid < BMB) load_terms(itr + 1);
+    }
+
+    // Each iteration handles the Q tile as two 32-row blocks and overlaps one
+    // block's matrix-core work with the other's vector work:
+    //   A: S, dP of block 0
+    //   B: S, dP of block 1            | P, dS of block 0
+    //   C: dV^T, dK^T += of block 0    | P, dS of block 1
+    //   D: dV^T, dK^T += of block 1
+    // (one wave per SIMD, so the overlap has to come from the wave's own
+    // instruction order; sched_barrier fences keep each step's pairing).
+    // Accumulator element i of a block is query row 8*(i/4) + 4*hf + (i%4)
+    // of the block, key my_key.
+    const bool masked = qt.cls != SAP_TILE_FULL || qt.n < BMB || kt.n < BNB;
+    // a row r sees this lane's key iff r >= rmin (causality; invalid keys see
+    // no row) and kg >= ds[r] (document start; INT_MIN unless PARTIAL)
+    const int rmin = key_ok ? kg - qt.global_start : (1 << 30);
+    const float *s_lse2 = reinterpret_cast<const float *>(cur + KS::LSE2);
+    const float *s_delta = reinterpret_cast<const float *>(cur + KS::DELTA);
+    const int *s_ds = reinterpret_cast<const int *>(cur + KS::DS);
+    auto row_op = [&](int tensor_off, int qb, int t) {   // A operand of S / dP, block qb, k-step t
+      return as_bf16x8(*reinterpret_cast<const u32x4 *>(cur + tensor_off + qb * 32 * RT::ROW + (r_off ^ (32 * t))));
+    };
+    auto iteration = [&](auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      f32x16 sacc[2], pacc[2];
+      bf16x8 pb[2][2], sb[2][2];
+      // P and dS of 4 elements (rows 8*g4 + 4*hf + 0..3 of block qb), packed
+      // into dword pairs of the B operands as soon as they exist
+      auto group4 = [&](int qb, int g4) {
+        const int r0 = qb * 32 + 8 * g4 + 4 * hf;
+        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(s_lse2 + r0);
+        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(s_delta + r0);
+        u32x4 dsv = {};
+        if (MASK) dsv = *reinterpret_cast<const u32x4 *>(s_ds + r0);
+        float pv[4], sv[4];
 #pragma unroll
-        for (int ps = 0; ps < PASSES; ++ps) {
-          const int idx = ps * NT + tid;
-          if (ITEMS % NT != 0 && idx >= ITEMS) break;
-          const int qgp = idx % NQG, dc = idx / NQG;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<u32x4 *>(lds + S::Q_ROW + (qgp * 4 + i) * S::RS + 8 * dc) = rq[ps][i];
-            *reinterpret_cast<u32x4 *>(lds + S::DO_ROW + (qgp * 4 + i) * S::RS + 8 * dc) = rd[ps][i];
-          }
-          const int col = ((qgp * 4) & ~15) | perm16((qgp * 4) & 15);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            *reinterpret_cast<u32x2 *>(lds + S::Q_T + (8 * dc + j) * S::TS + col) = gather4(rq[ps], j);
-            *reinterpret_cast<u32x2 *>(lds + S::DO_T + (8 * dc + j) * S::TS + col) = gather4(rd[ps], j);
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g4 + e;
+          float x = __builtin_fmaf(sacc[qb][i], c, -l4[e]);
+          if (MASK)          // masked pairs: exp2(-inf) = 0 (a select, not a branch)
+            x = ((r0 + e >= rmin) & (kg >= int(dsv[e]))) ? x : -INFINITY;
+          const float pr = __builtin_amdgcn_exp2f(x);
+          pv[e] = pr;
+          sv[e] = pr * (pacc[qb][i] - d4[e]);
         }
-        if (tid < BMB) {
-          const int row = min(tid, qt.n - 1);
-          const int64_t li = int64_t(h) * p.tq + qt.local_start + row;
-          const float l = p.lse[li];
-          // rows past the tile end or with no key at all get P = 0
-          s_lse2[tid] = (tid < qt.n && l != -INFINITY) ? l * LOG2E : INFINITY;
-          s_delta[tid] = p.delta[li];
-          // document start bounds keys only in PARTIAL tiles
-          s_ds[tid] = qt.cls == SAP_TILE_PARTIAL ? p.ds_q[qt.local_start + row] : INT_MIN;
+        // element i of the block sits in dword (i % 8) / 2 of B operand u = i / 8
+        const int u = g4 >> 1, w0 = 2 * (g4 & 1);
+        u32x4 pk = __builtin_bit_cast(u32x4, pb[qb][u]), sk = __builtin_bit_cast(u32x4, sb[qb][u]);
+        pk[w0] = pack_bf16(pv[0], pv[1]);
+        pk[w0 + 1] = pack_bf16(pv[2], pv[3]);
+        sk[w0] = pack_bf16(sv[0], sv[1]);
+        sk[w0 + 1] = pack_bf16(sv[2], sv[3]);
+        pb[qb][u] = as_bf16x8(pk);
+        sb[qb][u] = as_bf16x8(sk);
+      };
+      constexpr int NS = D / 16;           // k-steps of S / dP
+      constexpr int EPS = 16 / NS;         // elements of the other block per k-step
+
+      // ---- A: S, dP of block 0 (operands read one step ahead)
+      sacc[0] = pacc[0] = f32x16{};
+      sacc[1] = pacc[1] = f32x16{};
+      {
+        bf16x8 aq = row_op(KS::Q, 0, 0), ad = row_op(KS::DO, 0, 0);
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+          bf16x8 nq = aq, nd = ad;
+          if (t + 1 < NS) {
+            nq = row_op(KS::Q, 0, t + 1);
+            nd = row_op(KS::DO, 0, t + 1);
+          }
+          sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[t], sacc[0], 0, 0, 0);
+          pacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[t], pacc[0], 0, 0, 0);
+          aq = nq;
+          ad = nd;
         }
       }
-      if (itr + 1 < n_iter) load_rows(itr + 1);
-      __syncthreads();
-
-      // ---- S = Q K^T, dP = dO V^T (64 queries x this wave's 32 keys)
-      f32x16 sacc[2], pacc[2];
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- B: S, dP of block 1 | P, dS of block 0
+      {
+        bf16x8 aq = row_op(KS::Q, 1, 0), ad = row_op(KS::DO, 1, 0);
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+          bf16x8 nq = aq, nd = ad;
+          if (t + 1 < NS) {
+            nq = row_op(KS::Q, 1, t + 1);
+            nd = row_op(KS::DO, 1, t + 1);
+          }
+          sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[t], sacc[1], 0, 0, 0);
+          pacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[t], pacc[1], 0, 0, 0);
+          if ((t * EPS) % 4 == 0 && EPS <= 4) group4(0, (t * EPS) / 4);
+          if (EPS > 4)
+#pragma unroll
+            for (int j = 0; j < EPS / 4; ++j) group4(0, (t * EPS) / 4 + j);
+          aq = nq;
+          ad = nd;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- C: dV^T, dK^T of block 0 | P, dS of block 1; D: of block 1.
+      //      k-step (qb, u) covers rows qb*32 + 16u + 4hf + (0..3 | 8..11)
+      constexpr int NC = 2 * (D / 32);     // MFMA pairs per block
+      constexpr int EPC = 16 / NC;         // elements of block 1 per pair
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        sacc[qb] = f32x16{};
-        pacc[qb] = f32x16{};
+        bf16x8 ado = tr_pair(cur + KS::DO, qb * 32, 0), aqt = tr_pair(cur + KS::Q, qb * 32, 0);
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+          const int u = k / (D / 32), db = k % (D / 32);
+          bf16x8 n_do = ado, n_qt = aqt;
+          if (k + 1 < NC) {
+            const int u1 = (k + 1) / (D / 32), db1 = (k + 1) % (D / 32);
+            n_do = tr_pair(cur + KS::DO, qb * 32 + 16 * u1, db1);
+            n_qt = tr_pair(cur + KS::Q, qb * 32 + 16 * u1, db1);
+          }
+          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, pb[qb][u], dva[db], 0, 0, 0);
+          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, sb[qb][u], dka[db], 0, 0, 0);
+          if (qb == 0 && (k * EPC) % 4 == 0) group4(1, (k * EPC) / 4);
+          ado = n_do;
+          aqt = n_qt;
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-#pragma unroll
-      for (int t = 0; t < D / 16; ++t)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const int row = qb * 32 + l32;
-          const bf16x8 aq = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + S::Q_ROW + row * S::RS + 16 * t + 8 * hf));
-          const bf16x8 ad = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + S::DO_ROW + row * S::RS + 16 * t + 8 * hf));
-          sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[t], sacc[qb], 0, 0, 0);
-          pacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[t], pacc[qb], 0, 0, 0);
-        }
+    };
+    if (masked)
+      iteration(std::true_type{});
+    else
+      iteration(std::false_type{});
 
-      // ---- P and dS; accumulator element i of block qb is query row
-      //      qb*32 + 8*(i/4) + 4*hf + (i%4), key my_key. The per-row terms of a
-      //      lane's 16 rows come as four 4-row vector reads per block.
-      const bool masked = qt.cls != SAP_TILE_FULL || qt.n < BMB || kt.n < BNB;
-      // a row r sees this lane's key iff r >= rmin (causality; invalid keys see
-      // no row) and kg >= s_ds[r] (document start; INT_MIN unless PARTIAL)
-      const int rmin = key_ok ? kg - qt.global_start : (1 << 30);
-      bf16x8 pb[2][2], sb[2][2];
-      auto p_and_ds = [&](auto mask_tag) {
-        constexpr bool MASK = decltype(mask_tag)::value;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          f32x4 l4[4], d4[4];
-          int ds4[4][4];
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int r0 = qb * 32 + 8 * g4 + 4 * hf;
-            l4[g4] = *reinterpret_cast<const f32x4 *>(s_lse2 + r0);
-            d4[g4] = *reinterpret_cast<const f32x4 *>(s_delta + r0);
-            if (MASK) {
-              const u32x4 dsv = *reinterpret_cast<const u32x4 *>(s_ds + r0);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) ds4[g4][e] = int(dsv[e]);
-            }
-          }
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            float pv[8], sv[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const int i = 8 * u + j;
-              const int g4 = i >> 2, e = i & 3;
-              float x = __builtin_fmaf(sacc[qb][i], c, -l4[g4][e]);
-              if (MASK) {          // masked pairs: exp2(-inf) = 0 (a select, not a branch)
-                const int r = qb * 32 + 8 * g4 + 4 * hf + e;
-                x = ((r >= rmin) & (kg >= ds4[g4][e])) ? x : -INFINITY;
-              }
-              const float pr = __builtin_amdgcn_exp2f(x);
-              pv[j] = pr;
-              sv[j] = pr * (pacc[qb][i] - d4[g4][e]);
-            }
-            u32x4 pk, sk;
-            pk.x = pack_bf16(pv[0], pv[1]);
-            pk.y = pack_bf16(pv[2], pv[3]);
-            pk.z = pack_bf16(pv[4], pv[5]);
-            pk.w = pack_bf16(pv[6], pv[7]);
-            sk.x = pack_bf16(sv[0], sv[1]);
-            sk.y = pack_bf16(sv[2], sv[3]);
-            sk.z = pack_bf16(sv[4], sv[5]);
-            sk.w = pack_bf16(sv[6], sv[7]);
-            pb[qb][u] = as_bf16x8(pk);
-            sb[qb][u] = as_bf16x8(sk);
-          }
-        }
-      };
-      if (masked)
-        p_and_ds(std::true_type{});
-      else
-        p_and_ds(std::false_type{});
-
-      // ---- dV^T += dO^T P, dK^T += Q^T dS (k = 16 query rows per step)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const int off = (db * 32 + l32) * S::TS + qb * 32 + 16 * u + 8 * hf;
-            const bf16x8 ado = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + S::DO_T + off));
-            const bf16x8 aqt = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + S::Q_T + off));
-            dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, pb[qb][u], dva[db], 0, 0, 0);
-            dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, sb[qb][u], dka[db], 0, 0, 0);
-          }
-    }
+    // the next iteration's row terms (loaded above, latency hidden by the math)
+    if (more && tid < BMB) store_terms(nxt);
+    // copies for the next iteration have landed and every wave is done with this stage
+    __syncthreads();
   }
 
   if (!key_ok) return;

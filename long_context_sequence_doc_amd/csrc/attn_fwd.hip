@@ -156,7 +156,10 @@ __device__ inline unsigned pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(unsigned, v);
 }
 
-template <int D>
+// MERGE: o / lse hold a running result that this call's partial is merged
+// into (the ring step's merge folded into the epilogue), instead of being
+// overwritten.
+template <int D, bool MERGE>
 __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(FwdParams p) {
   using ST = Stage<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * ST::BYTES];
@@ -326,8 +329,33 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(FwdParams p) {
   if (!row_ok) return;
   const int row = wi.local_start + my_row;
   const bool empty = !(l > 0.f);
-  const float inv = empty ? 0.f : 1.f / l;
   float *op = p.o + (int64_t(row) * p.hq + h) * D + 4 * hf;
+  float *lp = p.lse + int64_t(h) * p.tq + row;
+  if (MERGE) {
+    // merge into the running (O, LSE) of the row:
+    //   L = ln(e^La + e^Lb), O = e^(La - L) O_a + e^(Lb - L) O_b
+    // a row with no key in this call keeps its running result
+    if (empty) return;
+    const float lb = m_used * p.scale + __logf(l);
+    const float la = *lp;                        // both lanes read before lane hf == 0 writes
+    const float mx = fmaxf(la, lb), mn = fminf(la, lb);
+    const float L = mx + log1pf(__expf(mn - mx));
+    const float wa = la == -INFINITY ? 0.f : __expf(la - L);
+    const float wb = __expf(lb - L) / l;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(op + db * 32 + 8 * ig);
+        f32x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = wa * a[e] + wb * oacc[db][4 * ig + e];
+        *reinterpret_cast<f32x4 *>(op + db * 32 + 8 * ig) = v4;
+      }
+    if (hf == 0) *lp = L;
+    return;
+  }
+  const float inv = empty ? 0.f : 1.f / l;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -339,7 +367,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(FwdParams p) {
       v4.w = oacc[db][4 * ig + 3] * inv;
       *reinterpret_cast<f32x4 *>(op + db * 32 + 8 * ig) = v4;
     }
-  if (hf == 0) p.lse[int64_t(h) * p.tq + row] = empty ? -INFINITY : m_used * p.scale + __logf(l);
+  if (hf == 0) *lp = empty ? -INFINITY : m_used * p.scale + __logf(l);
 }
 
 }  // namespace
@@ -369,10 +397,17 @@ hipError_t launch_attn_fwd(const FwdLaunch &a, hipStream_t stream) {
   // 32-bit row offsets inside a 64-row tile
   if (blocks > INT32_MAX || a.kv_row_stride > INT32_MAX / BN) return hipErrorInvalidValue;
   const dim3 grid{static_cast<unsigned>(blocks)}, block{NTHREADS};
-  if (a.d == 128)
-    hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, block, 0, stream, p);
-  else
-    hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, block, 0, stream, p);
+  if (a.d == 128) {
+    if (a.merge)
+      hipLaunchKernelGGL((attn_fwd_kernel<128, true>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_fwd_kernel<128, false>), grid, block, 0, stream, p);
+  } else {
+    if (a.merge)
+      hipLaunchKernelGGL((attn_fwd_kernel<64, true>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_fwd_kernel<64, false>), grid, block, 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -21,6 +21,7 @@ struct FwdLaunch {
   const PartnerEntry *partners;
   const int32_t *ds_q;
   int32_t n_work;
+  bool merge;         // o / lse are a running result to merge into
 };
 
 hipError_t launch_attn_fwd(const FwdLaunch &a, hipStream_t stream);

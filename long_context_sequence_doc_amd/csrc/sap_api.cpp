@@ -202,9 +202,11 @@ void sap_plan_free(sap_plan_t plan) {
   delete plan;
 }
 
-sap_status sap_attn_fwd(sap_plan_t plan, const void *q, const void *k, const void *v,
-                        int64_t q_row_stride, int64_t kv_row_stride, int32_t hq, int32_t hkv,
-                        int32_t d, float scale, float *o, float *lse, void *hip_stream) {
+namespace {
+
+sap_status fwd_impl(sap_plan_t plan, const void *q, const void *k, const void *v, int64_t q_row_stride,
+                    int64_t kv_row_stride, int32_t hq, int32_t hkv, int32_t d, float scale, float *o, float *lse,
+                    bool merge, void *hip_stream) {
   if (!plan) return fail(SAP_ERR_INVALID_ARG, "plan is NULL");
   sap_status s = check_heads(hq, hkv, d);
   if (s != SAP_OK) return s;
@@ -225,9 +227,24 @@ sap_status sap_attn_fwd(sap_plan_t plan, const void *q, const void *k, const voi
   a.o = o; a.lse = lse; a.tq = P.tq;
   a.work = P.dev.q_work; a.range = P.dev.q_range; a.partners = P.dev.q_partners; a.ds_q = P.dev.ds_q;
   a.n_work = int32_t(P.q_work.size());
+  a.merge = merge;
   hipError_t e = sap::launch_attn_fwd(a, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
   return ok();
+}
+
+}  // namespace
+
+sap_status sap_attn_fwd(sap_plan_t plan, const void *q, const void *k, const void *v,
+                        int64_t q_row_stride, int64_t kv_row_stride, int32_t hq, int32_t hkv,
+                        int32_t d, float scale, float *o, float *lse, void *hip_stream) {
+  return fwd_impl(plan, q, k, v, q_row_stride, kv_row_stride, hq, hkv, d, scale, o, lse, false, hip_stream);
+}
+
+sap_status sap_attn_fwd_merge(sap_plan_t plan, const void *q, const void *k, const void *v,
+                              int64_t q_row_stride, int64_t kv_row_stride, int32_t hq, int32_t hkv,
+                              int32_t d, float scale, float *o_acc, float *lse_acc, void *hip_stream) {
+  return fwd_impl(plan, q, k, v, q_row_stride, kv_row_stride, hq, hkv, d, scale, o_acc, lse_acc, true, hip_stream);
 }
 
 sap_status sap_lse_merge(sap_plan_t plan, float *o_acc, float *lse_acc, const float *o_part,

@@ -10,8 +10,12 @@ one rank's work is:
     step 0 (the rank's own chunks; every local row sees at least itself):
         sap_attn_fwd -> running O / LSE
     each later step whose plan lists any tile:
+        sap_attn_fwd_merge -> its partial merged into the running O / LSE in
+        the kernel epilogue (touched rows with a key only; the others are
+        exact as they are)
+      or, with fused_merge=False, the two-pass form:
         sap_attn_fwd -> partial O / LSE of the touched rows
-        sap_lse_merge   (touched rows only; the others are exact as they are)
+        sap_lse_merge   (touched rows only)
     steps with no tile launch nothing -- the sequence-aware part: with
     document masks most remote chunks of a rank hold no key its rows may see.
 
@@ -28,8 +32,9 @@ from typing import List, Sequence, Tuple
 
 import torch
 
-from . import (sap_attn_bwd_accumulate, sap_attn_bwd_rowterm, sap_attn_bwd_workspace, sap_attn_fwd, sap_lse_merge, sap_plan,
-               sap_plan_free, sap_plan_info, sap_plan_q_tiles, sap_plan_upload)
+from . import (sap_attn_bwd_accumulate, sap_attn_bwd_rowterm, sap_attn_bwd_workspace, sap_attn_fwd,
+               sap_attn_fwd_merge, sap_lse_merge, sap_plan, sap_plan_free, sap_plan_info, sap_plan_q_tiles,
+               sap_plan_upload)
 
 BLOCK_M, BLOCK_N = 128, 64
 
@@ -37,8 +42,9 @@ BLOCK_M, BLOCK_N = 128, 64
 class RankForward:
     def __init__(self, cu_seqlens, q_segs: Sequence[Tuple[int, int, int]],
                  step_kv_segs: List[Sequence[Tuple[int, int, int]]], hq: int, hkv: int, d: int,
-                 scale: float, device: str = "cuda"):
+                 scale: float, device: str = "cuda", fused_merge: bool = True):
         self.hq, self.hkv, self.d, self.scale = hq, hkv, d, scale
+        self.fused_merge = fused_merge
         self.plans = [sap_plan(cu_seqlens, q_segs, kv, BLOCK_M, BLOCK_N) for kv in step_kv_segs]
         self.infos = [sap_plan_info(p) for p in self.plans]
         first = self.infos[0]
@@ -50,7 +56,7 @@ class RankForward:
             sap_plan_upload(self.plans[i])
         self.o = torch.empty((self.tq, hq, d), dtype=torch.float32, device=device)
         self.lse = torch.empty((hq, self.tq), dtype=torch.float32, device=device)
-        need_part = len(self.active) > 1
+        need_part = len(self.active) > 1 and not fused_merge
         self.o_part = torch.empty_like(self.o) if need_part else None
         self.lse_part = torch.empty_like(self.lse) if need_part else None
 
@@ -83,6 +89,9 @@ class RankForward:
             if n == 0:
                 sap_attn_fwd(p, q, k, v, q_row_stride, kv_row_stride, self.hq, self.hkv, self.d, self.scale,
                              self.o, self.lse, stream)
+            elif self.fused_merge:
+                sap_attn_fwd_merge(p, q, k, v, q_row_stride, kv_row_stride, self.hq, self.hkv, self.d, self.scale,
+                                   self.o, self.lse, stream)
             else:
                 sap_attn_fwd(p, q, k, v, q_row_stride, kv_row_stride, self.hq, self.hkv, self.d, self.scale,
                              self.o_part, self.lse_part, stream)

@@ -128,12 +128,13 @@ def test_forward_is_deterministic():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
-def _rank_run(name):
+def _rank_run(name, fused_merge=True):
     import torch
     from long_context_sequence_doc_amd.rank import RankForward
     w = W.by_name(name)
     t = tensors(name)
-    rf = RankForward(w.cu, w.q_segs, [s.kv_segs for s in w.steps], w.hq, w.hkv, w.d, w.scale)
+    rf = RankForward(w.cu, w.q_segs, [s.kv_segs for s in w.steps], w.hq, w.hkv, w.d, w.scale,
+                     fused_merge=fused_merge)
     q = to_dev(W.local_rows(t.q, w.q_segs))
     k, v = to_dev(t.k), to_dev(t.v)
     rf.run(q, k, v, q.stride(0), k.stride(0))
@@ -145,8 +146,8 @@ def test_ring_rank_all_steps_and_merge():
     """32K ring, rank 3: step-by-step partials and the merged result, all rows."""
     sap = _sap()
     import torch
-    say("case ring_sp8_32k_rank3: 8 ring steps (2 non-empty) + merge")
-    w, t, rf, q, k, v = _rank_run("ring")
+    say("case ring_sp8_32k_rank3: 8 ring steps (2 non-empty) + merge pass")
+    w, t, rf, q, k, v = _rank_run("ring", fused_merge=False)
     assert rf.active == [0, 1]
     o, lse = rf.o.cpu().numpy(), rf.lse.cpu().numpy()
     gq = w.q_global_rows()
@@ -161,10 +162,74 @@ def test_ring_rank_all_steps_and_merge():
     rf.close()
 
 
-def test_zigzag_gqa_headline_sampled():
-    """128K zigzag GQA shard (rank 3), the benchmarked configuration; sampled rows."""
+def test_ring_rank_fused_merge():
+    """32K ring, rank 3, the merge folded into the forward epilogue: all rows,
+    and bit-for-bit the same rows untouched by step 1 as after step 0."""
     _sap()
-    say("case zigzag_sp8_128k_gqa_rank3: 3 non-empty steps + 2 merges, sampled rows")
+    import torch
+    say("case ring_sp8_32k_rank3: fused merge")
+    w, t, rf, q, k, v = _rank_run("ring", fused_merge=True)
+    assert rf.active == [0, 1] and rf.o_part is None
+    gq = w.q_global_rows()
+    ro, rl = A.forward(f64(W.local_rows(t.q, w.q_segs)), f64(t.k), f64(t.v), gq, np.arange(w.total), w.cu, w.scale)
+    compare(rf.o.cpu().numpy(), rf.lse.cpu().numpy(), ro, rl, label="ring fused merge")
+    rf.close()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_fused_merge_random(seed):
+    """sap_attn_fwd over KV part A, then sap_attn_fwd_merge over part B, against
+    the oracle over A and B together. Rows of touched tiles with no key in B
+    keep their values exactly; rows with no key in A (LSE -inf) take B's."""
+    sap = _sap()
+    import torch
+    rng = np.random.default_rng(100 + seed)
+    lengths = W.random_docs(rng, int(rng.integers(200, 900)), 300)
+    cu = W.cu_seqlens(lengths)
+    total = int(cu[-1])
+    hq, hkv, d = [(4, 2, 64), (2, 2, 128), (6, 3, 64), (4, 1, 128)][seed]
+    scale = 1.0 / np.sqrt(d)
+    rs = np.random.default_rng(200 + seed)
+    qb = W.bf16_round(rs.standard_normal((total, hq, d), dtype=np.float32))
+    kb = W.bf16_round(rs.standard_normal((total, hkv, d), dtype=np.float32))
+    vb = W.bf16_round(rs.standard_normal((total, hkv, d), dtype=np.float32))
+    cut = int(rng.integers(1, total))
+    segs_a, segs_b = [(0, cut, 0)], [(cut, total, cut)]
+    if seed % 2:
+        segs_a, segs_b = segs_b, segs_a
+    q_segs = [(0, total, 0)]
+    say(f"case fused merge seed {seed}: T={total} docs={len(lengths)} cut={cut} hq={hq} hkv={hkv} d={d}")
+    pa = sap.sap_plan(cu, q_segs, segs_a, 128, 64)
+    pb = sap.sap_plan(cu, q_segs, segs_b, 128, 64)
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    o = torch.zeros((total, hq, d), device="cuda")
+    lse = torch.full((hq, total), float("-inf"), device="cuda")
+    for p in (pa, pb):
+        if sap.sap_plan_info(p)["n_tiles"]:
+            sap.sap_plan_upload(p)
+    sap.sap_attn_fwd(pa, q, k, v, q.stride(0), k.stride(0), hq, hkv, d, scale, o, lse)
+    torch.cuda.synchronize()
+    o_a, l_a = o.cpu().numpy().copy(), lse.cpu().numpy().copy()
+    sap.sap_attn_fwd_merge(pb, q, k, v, q.stride(0), k.stride(0), hq, hkv, d, scale, o, lse)
+    torch.cuda.synchronize()
+    g = np.arange(total)
+    ro, rl = A.forward(f64(qb), f64(kb), f64(vb), g, g, cu, scale)
+    compare(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, label=f"fused merge seed {seed}")
+    # rows with no key in B: unchanged, bit for bit
+    gb = np.concatenate([np.arange(a, b) for a, b, _ in segs_b])
+    _, rl_b = A.forward(f64(qb), f64(kb[gb]), f64(vb[gb]), g, gb, cu, scale)
+    keep = np.isneginf(rl_b)
+    assert np.array_equal(o.cpu().numpy().transpose(1, 0, 2)[keep], o_a.transpose(1, 0, 2)[keep])
+    assert np.array_equal(lse.cpu().numpy()[keep], l_a[keep])
+    sap.sap_plan_free(pa)
+    sap.sap_plan_free(pb)
+
+
+def test_zigzag_gqa_headline_sampled():
+    """128K zigzag GQA shard (rank 3), the benchmarked configuration (merges
+    folded into the forward); sampled rows."""
+    _sap()
+    say("case zigzag_sp8_128k_gqa_rank3: 3 non-empty steps, fused merges, sampled rows")
     w, t, rf, q, k, v = _rank_run("zigzag")
     assert rf.active == [0, 1, 7]
     gq = w.q_global_rows()
