@@ -63,7 +63,6 @@ typedef __attribute__((address_space(1))) void global_void;
 constexpr int BMB = 64;     // query rows per Q tile
 constexpr int BNB = 128;    // keys per KV tile
 constexpr int NT = 256;     // threads of the KV kernel
-constexpr int NTQ = 128;    // threads of the dQ kernel
 constexpr int NXCD = 8;
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -497,36 +496,40 @@ __global__ __launch_bounds__(NT) void bwd_kv_reduce_kernel(const ReduceItem *ite
 // ---------------------------------------------------------------------------
 constexpr int HK = 64;      // keys per half of a KV tile in the dQ kernel
 
-template <int D>
-struct DqSmem {
-  static constexpr int RS = D + 8;            // row-major K / V row stride (elements)
-  static constexpr int TS = HK + 8;           // transposed K row stride
-  static constexpr int K_ROW = 0;
-  static constexpr int V_ROW = K_ROW + HK * RS;
-  static constexpr int K_T = V_ROW + HK * RS;
-  static constexpr int ELEMS = K_T + D * TS;
-};
+// dQ kernel: one workgroup = one 64-row Q tile x NH query heads of one KV
+// head (NH = 2 when the GQA group has an even size, so four waves share each
+// staged K / V half-tile). Wave w owns head hq0 + w / 2, rows 32 (w % 2) ..
+// +31. Per 64-key half of a partner KV tile, staged by direct copies into a
+// double-buffered LDS stage (K rows, V rows; swizzled as RowTile):
+//   S^T = K Q^T, dP^T = V dO^T            (A: K / V rows, B: Q / dO in registers)
+//   dS^T = P^T o (dP^T - D)               (one query per lane pair: LSE, D scalars)
+//   dQ^T += K^T dS^T                      (A: K^T by transposing reads of K rows)
+template <int D, int NH>
+__global__ __launch_bounds__(128 * NH) void attn_bwd_dq_kernel(BwdParams p) {
+  using RT = RowTile<D>;
+  constexpr int NTD = 128 * NH;                      // threads
+  constexpr int NWV = 2 * NH;                        // waves
+  constexpr int KOFF = 0, VOFF = RT::BYTES;          // K, V half-tiles (HK == BMB rows)
+  constexpr int STAGE = 2 * RT::BYTES;
+  static_assert(HK == BMB, "the K / V half-tiles reuse the 64-row tile geometry");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * STAGE];
 
-template <int D>
-__global__ __launch_bounds__(NTQ) void attn_bwd_dq_kernel(BwdParams p) {
-  using S = DqSmem<D>;
-  __shared__ __attribute__((aligned(16))) unsigned short lds[S::ELEMS];
-
-  // workgroup -> (Q tile, query head); the heads of one KV head and
+  // workgroup -> (Q tile, head pair); the head pairs of one KV head and
   // consecutive Q tiles of one KV head go to the same XCD (ids are dealt
   // round-robin over the XCDs), to share K / V in its L2
+  const int pairs = p.group / NH;
   const int b = blockIdx.x;
   const int xcd = b % NXCD, slot = b / NXCD;
-  const int G = (slot / p.group) * NXCD + xcd;
+  const int G = (slot / pairs) * NXCD + xcd;
   if (G >= p.n_work * p.hkv) return;
   const int w = G / p.hkv, g = G % p.hkv;
-  const int h = g * p.group + slot % p.group;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int h = g * p.group + (slot % pairs) * NH + wave / 2;
   const WorkItem qt = p.work[w];
   const WorkRange rg = p.range[w];
 
-  const int my_row = wave * 32 + l32;             // query row within the Q tile
+  const int my_row = (wave & 1) * 32 + l32;       // query row within the Q tile
   const bool row_ok = my_row < qt.n;
   const int qrow = qt.local_start + min(my_row, qt.n - 1);
   const int qg = qt.global_start + my_row;
@@ -551,102 +554,125 @@ __global__ __launch_bounds__(NTQ) void attn_bwd_dq_kernel(BwdParams p) {
   for (int i = 0; i < D / 32; ++i) qacc[i] = f32x16{};
   const float c = p.c;
 
-  for (int it = 0; it < rg.count; ++it) {
-    const PartnerEntry kt = p.partners[rg.begin + it];
-    for (int half = 0; half * HK < kt.n; ++half) {
-      const int k0 = half * HK;                   // first key of this half within the tile
-      const int kn = min(HK, kt.n - k0);          // keys in this half
-      __syncthreads();   // previous half done with the K / V buffers
-      // ---- stage K rows, V rows and K^T (key-permuted) for 64 keys
-      {
-        constexpr int NKG = HK / 4;               // 16 groups of 4 keys
-        constexpr int ITEMS = NKG * (D / 8);
-        static_assert(ITEMS % NTQ == 0, "staging assumes whole passes");
-        const int64_t base = int64_t(kt.local_start + k0) * p.kv_row_stride + int64_t(g) * D;
+  // copy geometry of a half-tile (see RowTile): chunk position
+  // P = (i * NWV + wave) * 64 + lane holds row P / CPR, chunk (P % CPR) ^ sw(row)
+  constexpr int LOADS = HK * RT::CPR / NTD;
+  static_assert(LOADS * NTD == HK * RT::CPR, "copies must split evenly");
+  int src_row[LOADS], src_col[LOADS];
 #pragma unroll
-        for (int ps = 0; ps < ITEMS / NTQ; ++ps) {
-          const int idx = ps * NTQ + tid;
-          const int kgp = idx % NKG, dc = idx / NKG;
-          u32x4 rk[4], rv[4];
+  for (int i = 0; i < LOADS; ++i) {
+    const int P = (i * NWV + wave) * 64 + lane;
+    src_row[i] = P / RT::CPR;
+    src_col[i] = 8 * ((P % RT::CPR) ^ RT::sw(P / RT::CPR));
+  }
+  const int r_off = l32 * RT::ROW + 16 * (hf ^ RT::sw(l32));
+  int t_off[D / 32];
+  {
+    const int q4 = lane >> 4, s16 = lane & 15;
+    const int row = 4 * (q4 >> 1) + (s16 >> 2);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = min(kgp * 4 + i, kn - 1);
-            const int64_t off = base + int64_t(row) * p.kv_row_stride + 8 * dc;
-            rk[i] = *reinterpret_cast<const u32x4 *>(p.k + off);
-            rv[i] = *reinterpret_cast<const u32x4 *>(p.v + off);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<u32x4 *>(lds + S::K_ROW + (kgp * 4 + i) * S::RS + 8 * dc) = rk[i];
-            *reinterpret_cast<u32x4 *>(lds + S::V_ROW + (kgp * 4 + i) * S::RS + 8 * dc) = rv[i];
-          }
-          const int col = ((kgp * 4) & ~15) | perm16((kgp * 4) & 15);
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            *reinterpret_cast<u32x2 *>(lds + S::K_T + (8 * dc + j) * S::TS + col) = gather4(rk, j);
-        }
-      }
-      __syncthreads();
-
-      // ---- S^T = K Q^T, dP^T = V dO^T (64 keys x this wave's 32 queries)
-      f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int t = 0; t < D / 16; ++t)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int off = (kb * 32 + l32) * S::RS + 16 * t + 8 * hf;
-          const bf16x8 ak = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + S::K_ROW + off));
-          const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + S::V_ROW + off));
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[t], sacc[kb], 0, 0, 0);
-          pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[t], pacc[kb], 0, 0, 0);
-        }
-
-      // ---- dS^T = P^T o (dP^T - D); element i of key block kb is key
-      //      k0 + kb*32 + 8*(i/4) + 4*hf + (i%4) of the tile
-      const bool masked = kt.cls != SAP_TILE_FULL || kn < HK || qt.n < BMB;
-      int lo = -(1 << 30), hi = kn - 1;           // allowed half-local key range of this query
-      if (masked) {
-        if (kt.cls != SAP_TILE_FULL) hi = min(hi, qg - (kt.global_start + k0));
-        if (kt.cls == SAP_TILE_PARTIAL) lo = dsq - (kt.global_start + k0);
-      }
-      const int hi_r = hi - 4 * hf, lo_r = lo - 4 * hf;
-      bf16x8 sb[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          float sv[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int i = 8 * u + j;
-            float x = __builtin_fmaf(sacc[kb][i], c, -lse2);
-            if (masked) {            // masked pairs: exp2(-inf) = 0 (a select, not a branch)
-              const int kc = kb * 32 + 8 * (i >> 2) + (i & 3);
-              x = (kc <= hi_r && kc >= lo_r) ? x : -INFINITY;
-            }
-            const float pr = __builtin_amdgcn_exp2f(x);
-            sv[j] = pr * (pacc[kb][i] - dlt);
-          }
-          u32x4 sk;
-          sk.x = pack_bf16(sv[0], sv[1]);
-          sk.y = pack_bf16(sv[2], sv[3]);
-          sk.z = pack_bf16(sv[4], sv[5]);
-          sk.w = pack_bf16(sv[6], sv[7]);
-          sb[kb][u] = as_bf16x8(sk);
-        }
-
-      // ---- dQ^T += K^T dS^T (k = 16 keys per step; the D/32 blocks are independent chains)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(
-                lds + S::K_T + (db * 32 + l32) * S::TS + kb * 32 + 16 * u + 8 * hf));
-            qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb[kb][u], qacc[db], 0, 0, 0);
-          }
+    for (int db = 0; db < D / 32; ++db) {
+      const int col = db * 32 + 16 * (q4 & 1) + 4 * (s16 & 3);
+      t_off[db] = row * RT::ROW + 16 * ((col >> 3) ^ RT::sw(row)) + 2 * (col & 7);
     }
+  }
+  auto issue_half = [&](const PartnerEntry &kt, int half, unsigned char *stage) {
+    const int kn = min(HK, kt.n - half * HK);
+    const int64_t base = int64_t(kt.local_start + half * HK) * p.kv_row_stride + int64_t(g) * D;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int64_t off = base + int64_t(min(src_row[i], kn - 1)) * p.kv_row_stride + src_col[i];
+      const int dst = (i * NWV + wave) * 1024;
+      __builtin_amdgcn_global_load_lds((global_void *)(p.k + off), (lds_void *)(stage + KOFF + dst), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_void *)(p.v + off), (lds_void *)(stage + VOFF + dst), 16, 0, 0);
+    }
+  };
+
+  // iterations: the 64-key halves of the partner tiles, in order
+  int it = 0, half = 0, stage_i = 0;
+  if (rg.count > 0) issue_half(p.partners[rg.begin], 0, lds);
+  __syncthreads();
+  while (it < rg.count) {
+    const PartnerEntry kt = p.partners[rg.begin + it];
+    unsigned char *cur = lds + stage_i * STAGE;
+    // the next half: this tile's second one, or the next tile's first
+    int nit = it, nhalf = half + 1;
+    if (nhalf * HK >= kt.n) {
+      nit = it + 1;
+      nhalf = 0;
+    }
+    if (nit < rg.count) issue_half(p.partners[rg.begin + nit], nhalf, lds + (stage_i ^ 1) * STAGE);
+
+    const int k0 = half * HK;                     // first key of this half within the tile
+    const int kn = min(HK, kt.n - k0);            // keys in this half
+
+    // ---- S^T = K Q^T, dP^T = V dO^T (64 keys x this wave's 32 queries)
+    f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int off = kb * 32 * RT::ROW + (r_off ^ (32 * t));
+        const bf16x8 ak = as_bf16x8(*reinterpret_cast<const u32x4 *>(cur + KOFF + off));
+        const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(cur + VOFF + off));
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[t], sacc[kb], 0, 0, 0);
+        pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[t], pacc[kb], 0, 0, 0);
+      }
+
+    // ---- dS^T = P^T o (dP^T - D); element i of key block kb is key
+    //      k0 + kb*32 + 8*(i/4) + 4*hf + (i%4) of the tile
+    const bool masked = kt.cls != SAP_TILE_FULL || kn < HK || qt.n < BMB;
+    int lo = -(1 << 30), hi = kn - 1;             // allowed half-local key range of this query
+    if (masked) {
+      if (kt.cls != SAP_TILE_FULL) hi = min(hi, qg - (kt.global_start + k0));
+      if (kt.cls == SAP_TILE_PARTIAL) lo = dsq - (kt.global_start + k0);
+    }
+    const int hi_r = hi - 4 * hf, lo_r = lo - 4 * hf;
+    bf16x8 sb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float sv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = 8 * u + j;
+          float x = __builtin_fmaf(sacc[kb][i], c, -lse2);
+          const int kc = kb * 32 + 8 * (i >> 2) + (i & 3);
+          x = (kc <= hi_r && kc >= lo_r) ? x : -INFINITY;    // masked pairs: exp2(-inf) = 0
+          const float pr = __builtin_amdgcn_exp2f(x);
+          sv[j] = pr * (pacc[kb][i] - dlt);
+        }
+        u32x4 sk;
+        sk.x = pack_bf16(sv[0], sv[1]);
+        sk.y = pack_bf16(sv[2], sv[3]);
+        sk.z = pack_bf16(sv[4], sv[5]);
+        sk.w = pack_bf16(sv[6], sv[7]);
+        sb[kb][u] = as_bf16x8(sk);
+      }
+
+    // ---- dQ^T += K^T dS^T (k = 16 keys per step: kb*32 + 16u + 4hf + (0..3 | 8..11))
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const unsigned char *a = cur + KOFF + t_off[db] + (kb * 32 + 16 * u) * RT::ROW;
+          const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a));
+          const unsigned char *a8 = RT::CPR >= 16
+              ? cur + KOFF + ((t_off[db] ^ 128) + (kb * 32 + 16 * u + 8) * RT::ROW)
+              : a + 8 * RT::ROW;
+          const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a8));
+          const bf16x8 ak = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+          qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, sb[kb][u], qacc[db], 0, 0, 0);
+        }
+
+    // the next half's copies have landed and every wave is done with this stage
+    __syncthreads();
+    stage_i ^= 1;
+    it = nit;
+    half = nhalf;
   }
 
   // ---- dQ += scale dQ^T for this lane's query row
@@ -727,14 +753,22 @@ hipError_t launch_attn_bwd(const BwdLaunch &a, hipStream_t stream) {
     p.range = a.q_range;
     p.partners = a.q_partners;
     p.n_work = a.n_q_work;
+    const int nh = p.group % 2 == 0 ? 2 : 1;      // query heads per workgroup
     const int64_t slots = (int64_t(a.n_q_work) * a.hkv + NXCD - 1) / NXCD;
-    const int64_t blocks = slots * NXCD * p.group;
+    const int64_t blocks = slots * NXCD * (p.group / nh);
     if (blocks > INT32_MAX) return hipErrorInvalidValue;
     const dim3 grid{static_cast<unsigned>(blocks)};
-    if (a.d == 128)
-      hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, grid, dim3(NTQ), 0, stream, p);
-    else
-      hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, grid, dim3(NTQ), 0, stream, p);
+    if (a.d == 128) {
+      if (nh == 2)
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 2>), grid, dim3(256), 0, stream, p);
+      else
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 1>), grid, dim3(128), 0, stream, p);
+    } else {
+      if (nh == 2)
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 2>), grid, dim3(256), 0, stream, p);
+      else
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 1>), grid, dim3(128), 0, stream, p);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
