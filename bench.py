@@ -69,12 +69,13 @@ def _traffic_from_profiles(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, t, forward_only: bool, budget_s: float = 30.0):
-    """The oracle, as it stands, on a bounded sample of the same workload: the
-    query heads of KV head 0 over this rank's rows, every non-empty ring step
+def cpu_baseline(w, t, forward_only: bool, min_s: float = 10.0, budget_s: float = 30.0):
+    """The oracle, as it stands, on a bounded sample of the same workload: for
+    KV heads 0, 1, ... (until about min_s of work, or budget_s), the query
+    heads of that KV head over this rank's rows, every non-empty ring step
     (forward per step; then, unless forward-only, the oracle forward over all
-    KV rows for the final O / LSE and the backward per step). Rate = the
-    sample's allowed-pair FLOP (4 D forward + 10 D backward per pair and
+    KV rows for the final O / LSE, untimed, and the backward per step). Rate =
+    the sample's allowed-pair FLOP (4 D forward + 10 D backward per pair and
     query head) / wall time."""
     from oracle import attention as A
     from oracle import planner as P
@@ -84,42 +85,41 @@ def cpu_baseline(w, t, forward_only: bool, budget_s: float = 30.0):
         cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         cores = 1
-    heads = list(range(w.hq // w.hkv))           # query heads of KV head 0
-    q = W.bf16_to_f32(W.local_rows(t.q, w.q_segs)[:, heads]).astype(np.float64)
-    k = W.bf16_to_f32(t.k[:, :1]).astype(np.float64)
-    v = W.bf16_to_f32(t.v[:, :1]).astype(np.float64)
+    group = w.hq // w.hkv
     gq = w.q_global_rows()
-    pairs, steps_done, flop = 0, 0, 0.0
-    t0 = time.perf_counter()
-    steps = []
+    plans = []
     for st in w.steps:
-        gk = np.concatenate([np.arange(a, b) for a, b, _ in st.kv_segs])
         pl = P.plan(w.cu, w.q_segs, st.kv_segs, 128, 64)
-        if pl.n_tiles == 0:
-            continue
-        A.forward(q, k[gk], v[gk], gq, gk, w.cu, w.scale)
-        flop += 4.0 * w.d * len(heads) * pl.useful_pairs
-        steps.append((gk, pl.useful_pairs))
-        steps_done += 1
-        if time.perf_counter() - t0 > budget_s:
+        if pl.n_tiles:
+            plans.append((np.concatenate([np.arange(a, b) for a, b, _ in st.kv_segs]), pl.useful_pairs))
+    flop, timed, kv_heads = 0.0, 0.0, 0
+    for g in range(w.hkv):
+        heads = list(range(g * group, (g + 1) * group))
+        q = W.bf16_to_f32(W.local_rows(t.q, w.q_segs)[:, heads]).astype(np.float64)
+        k = W.bf16_to_f32(t.k[:, g:g + 1]).astype(np.float64)
+        v = W.bf16_to_f32(t.v[:, g:g + 1]).astype(np.float64)
+        t0 = time.perf_counter()
+        for gk, pr in plans:
+            A.forward(q, k[gk], v[gk], gq, gk, w.cu, w.scale)
+            flop += 4.0 * w.d * group * pr
+        timed += time.perf_counter() - t0
+        if not forward_only:
+            do = W.bf16_to_f32(W.local_rows(t.do, w.q_segs)[:, heads]).astype(np.float64)
+            o, lse = A.forward(q, k, v, gq, np.arange(w.total), w.cu, w.scale)   # inputs, not timed
+            t0 = time.perf_counter()
+            for gk, pr in plans:
+                A.backward(q, k[gk], v[gk], do, o, lse, gq, gk, w.cu, w.scale)
+                flop += 10.0 * w.d * group * pr
+            timed += time.perf_counter() - t0
+        kv_heads += 1
+        if timed >= min_s or timed * (kv_heads + 1) / kv_heads > budget_s:
             break
-    bwd_steps = 0
-    if not forward_only:
-        do = W.bf16_to_f32(W.local_rows(t.do, w.q_segs)[:, heads]).astype(np.float64)
-        allk = np.arange(w.total)
-        t1 = time.perf_counter()
-        o, lse = A.forward(q, k, v, gq, allk, w.cu, w.scale)
-        t0 += time.perf_counter() - t1      # the final O / LSE are inputs here, not timed work
-        for gk, pr in steps:
-            A.backward(q, k[gk], v[gk], do, o, lse, gq, gk, w.cu, w.scale)
-            flop += 10.0 * w.d * len(heads) * pr
-            bwd_steps += 1
-    dt = time.perf_counter() - t0
     what = "forward per step" if forward_only else \
-        f"forward per step, then backward for {bwd_steps} steps from the oracle's final O/LSE (not timed)"
-    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{w.name}: query heads 0-{len(heads) - 1} (KV head 0), all {w.tq} local rows, "
-                      f"{steps_done} non-empty ring steps ({what}); fp64 NumPy; {dt:.1f} s wall"}
+        "forward per step, then the backward per step from the oracle's final O/LSE (computed untimed)"
+    return {"value": flop / timed / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{w.name}: KV heads 0-{kv_heads - 1} with their {group * kv_heads} query heads, all "
+                      f"{w.tq} local rows, {len(plans)} non-empty ring steps ({what}); fp64 NumPy; "
+                      f"{timed:.1f} s timed"}
 
 
 class _Timer:

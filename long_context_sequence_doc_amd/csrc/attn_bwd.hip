@@ -286,16 +286,27 @@ __global__ __launch_bounds__(NT) void attn_bwd_kv_kernel(BwdParams p) {
       if (tid < BMB) load_terms(itr + 1);
     }
 
-    // Each iteration handles the Q tile as two 32-row blocks and overlaps one
-    // block's matrix-core work with the other's vector work:
-    //   A: S, dP of block 0
-    //   B: S, dP of block 1            | P, dS of block 0
-    //   C: dV^T, dK^T += of block 0    | P, dS of block 1
-    //   D: dV^T, dK^T += of block 1
-    // (one wave per SIMD, so the overlap has to come from the wave's own
-    // instruction order; sched_barrier fences keep each step's pairing).
-    // Accumulator element i of a block is query row 8*(i/4) + 4*hf + (i%4)
-    // of the block, key my_key.
+    // ---- S = Q K^T, dP = dO V^T (64 queries x this wave's 32 keys)
+    f32x16 sacc[2], pacc[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      sacc[qb] = f32x16{};
+      pacc[qb] = f32x16{};
+    }
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int off = qb * 32 * RT::ROW + (r_off ^ (32 * t));
+        const bf16x8 aq = as_bf16x8(*reinterpret_cast<const u32x4 *>(cur + KS::Q + off));
+        const bf16x8 ad = as_bf16x8(*reinterpret_cast<const u32x4 *>(cur + KS::DO + off));
+        sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[t], sacc[qb], 0, 0, 0);
+        pacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[t], pacc[qb], 0, 0, 0);
+      }
+
+    // ---- P and dS; accumulator element i of block qb is query row
+    //      qb*32 + 8*(i/4) + 4*hf + (i%4), key my_key. The per-row terms of a
+    //      lane's 16 rows come as four 4-row vector reads per block.
     const bool masked = qt.cls != SAP_TILE_FULL || qt.n < BMB || kt.n < BNB;
     // a row r sees this lane's key iff r >= rmin (causality; invalid keys see
     // no row) and kg >= ds[r] (document start; INT_MIN unless PARTIAL)
@@ -303,115 +314,72 @@ __global__ __launch_bounds__(NT) void attn_bwd_kv_kernel(BwdParams p) {
     const float *s_lse2 = reinterpret_cast<const float *>(cur + KS::LSE2);
     const float *s_delta = reinterpret_cast<const float *>(cur + KS::DELTA);
     const int *s_ds = reinterpret_cast<const int *>(cur + KS::DS);
-    auto row_op = [&](int tensor_off, int qb, int t) {   // A operand of S / dP, block qb, k-step t
-      return as_bf16x8(*reinterpret_cast<const u32x4 *>(cur + tensor_off + qb * 32 * RT::ROW + (r_off ^ (32 * t))));
-    };
-    auto iteration = [&](auto mask_tag) {
+    bf16x8 pb[2][2], sb[2][2];
+    auto p_and_ds = [&](auto mask_tag) {
       constexpr bool MASK = decltype(mask_tag)::value;
-      f32x16 sacc[2], pacc[2];
-      bf16x8 pb[2][2], sb[2][2];
-      // P and dS of 4 elements (rows 8*g4 + 4*hf + 0..3 of block qb), packed
-      // into dword pairs of the B operands as soon as they exist
-      auto group4 = [&](int qb, int g4) {
-        const int r0 = qb * 32 + 8 * g4 + 4 * hf;
-        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(s_lse2 + r0);
-        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(s_delta + r0);
-        u32x4 dsv = {};
-        if (MASK) dsv = *reinterpret_cast<const u32x4 *>(s_ds + r0);
-        float pv[4], sv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * g4 + e;
-          float x = __builtin_fmaf(sacc[qb][i], c, -l4[e]);
-          if (MASK)          // masked pairs: exp2(-inf) = 0 (a select, not a branch)
-            x = ((r0 + e >= rmin) & (kg >= int(dsv[e]))) ? x : -INFINITY;
-          const float pr = __builtin_amdgcn_exp2f(x);
-          pv[e] = pr;
-          sv[e] = pr * (pacc[qb][i] - d4[e]);
-        }
-        // element i of the block sits in dword (i % 8) / 2 of B operand u = i / 8
-        const int u = g4 >> 1, w0 = 2 * (g4 & 1);
-        u32x4 pk = __builtin_bit_cast(u32x4, pb[qb][u]), sk = __builtin_bit_cast(u32x4, sb[qb][u]);
-        pk[w0] = pack_bf16(pv[0], pv[1]);
-        pk[w0 + 1] = pack_bf16(pv[2], pv[3]);
-        sk[w0] = pack_bf16(sv[0], sv[1]);
-        sk[w0 + 1] = pack_bf16(sv[2], sv[3]);
-        pb[qb][u] = as_bf16x8(pk);
-        sb[qb][u] = as_bf16x8(sk);
-      };
-      constexpr int NS = D / 16;           // k-steps of S / dP
-      constexpr int EPS = 16 / NS;         // elements of the other block per k-step
-
-      // ---- A: S, dP of block 0 (operands read one step ahead)
-      sacc[0] = pacc[0] = f32x16{};
-      sacc[1] = pacc[1] = f32x16{};
-      {
-        bf16x8 aq = row_op(KS::Q, 0, 0), ad = row_op(KS::DO, 0, 0);
-#pragma unroll
-        for (int t = 0; t < NS; ++t) {
-          bf16x8 nq = aq, nd = ad;
-          if (t + 1 < NS) {
-            nq = row_op(KS::Q, 0, t + 1);
-            nd = row_op(KS::DO, 0, t + 1);
-          }
-          sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[t], sacc[0], 0, 0, 0);
-          pacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[t], pacc[0], 0, 0, 0);
-          aq = nq;
-          ad = nd;
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // ---- B: S, dP of block 1 | P, dS of block 0
-      {
-        bf16x8 aq = row_op(KS::Q, 1, 0), ad = row_op(KS::DO, 1, 0);
-#pragma unroll
-        for (int t = 0; t < NS; ++t) {
-          bf16x8 nq = aq, nd = ad;
-          if (t + 1 < NS) {
-            nq = row_op(KS::Q, 1, t + 1);
-            nd = row_op(KS::DO, 1, t + 1);
-          }
-          sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[t], sacc[1], 0, 0, 0);
-          pacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[t], pacc[1], 0, 0, 0);
-          if ((t * EPS) % 4 == 0 && EPS <= 4) group4(0, (t * EPS) / 4);
-          if (EPS > 4)
-#pragma unroll
-            for (int j = 0; j < EPS / 4; ++j) group4(0, (t * EPS) / 4 + j);
-          aq = nq;
-          ad = nd;
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // ---- C: dV^T, dK^T of block 0 | P, dS of block 1; D: of block 1.
-      //      k-step (qb, u) covers rows qb*32 + 16u + 4hf + (0..3 | 8..11)
-      constexpr int NC = 2 * (D / 32);     // MFMA pairs per block
-      constexpr int EPC = 16 / NC;         // elements of block 1 per pair
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        bf16x8 ado = tr_pair(cur + KS::DO, qb * 32, 0), aqt = tr_pair(cur + KS::Q, qb * 32, 0);
+        f32x4 l4[4], d4[4];
+        int ds4[4][4];
 #pragma unroll
-        for (int k = 0; k < NC; ++k) {
-          const int u = k / (D / 32), db = k % (D / 32);
-          bf16x8 n_do = ado, n_qt = aqt;
-          if (k + 1 < NC) {
-            const int u1 = (k + 1) / (D / 32), db1 = (k + 1) % (D / 32);
-            n_do = tr_pair(cur + KS::DO, qb * 32 + 16 * u1, db1);
-            n_qt = tr_pair(cur + KS::Q, qb * 32 + 16 * u1, db1);
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int r0 = qb * 32 + 8 * g4 + 4 * hf;
+          l4[g4] = *reinterpret_cast<const f32x4 *>(s_lse2 + r0);
+          d4[g4] = *reinterpret_cast<const f32x4 *>(s_delta + r0);
+          if (MASK) {
+            const u32x4 dsv = *reinterpret_cast<const u32x4 *>(s_ds + r0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ds4[g4][e] = int(dsv[e]);
           }
-          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, pb[qb][u], dva[db], 0, 0, 0);
-          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, sb[qb][u], dka[db], 0, 0, 0);
-          if (qb == 0 && (k * EPC) % 4 == 0) group4(1, (k * EPC) / 4);
-          ado = n_do;
-          aqt = n_qt;
-          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          float pv[8], sv[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int i = 8 * u + j;
+            const int g4 = i >> 2, e = i & 3;
+            float x = __builtin_fmaf(sacc[qb][i], c, -l4[g4][e]);
+            if (MASK) {          // masked pairs: exp2(-inf) = 0 (a select, not a branch)
+              const int r = qb * 32 + 8 * g4 + 4 * hf + e;
+              x = ((r >= rmin) & (kg >= ds4[g4][e])) ? x : -INFINITY;
+            }
+            const float pr = __builtin_amdgcn_exp2f(x);
+            pv[j] = pr;
+            sv[j] = pr * (pacc[qb][i] - d4[g4][e]);
+          }
+          u32x4 pk, sk;
+          pk.x = pack_bf16(pv[0], pv[1]);
+          pk.y = pack_bf16(pv[2], pv[3]);
+          pk.z = pack_bf16(pv[4], pv[5]);
+          pk.w = pack_bf16(pv[6], pv[7]);
+          sk.x = pack_bf16(sv[0], sv[1]);
+          sk.y = pack_bf16(sv[2], sv[3]);
+          sk.z = pack_bf16(sv[4], sv[5]);
+          sk.w = pack_bf16(sv[6], sv[7]);
+          pb[qb][u] = as_bf16x8(pk);
+          sb[qb][u] = as_bf16x8(sk);
         }
       }
     };
     if (masked)
-      iteration(std::true_type{});
+      p_and_ds(std::true_type{});
     else
-      iteration(std::false_type{});
+      p_and_ds(std::false_type{});
+
+    // ---- dV^T += dO^T P, dK^T += Q^T dS (k = 16 query rows per step; the
+    //      rows of k-step (qb, u) are qb*32 + 16u + 4hf + (0..3 | 8..11))
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const bf16x8 ado = tr_pair(cur + KS::DO, qb * 32 + 16 * u, db);
+          const bf16x8 aqt = tr_pair(cur + KS::Q, qb * 32 + 16 * u, db);
+          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, pb[qb][u], dva[db], 0, 0, 0);
+          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, sb[qb][u], dka[db], 0, 0, 0);
+        }
 
     // the next iteration's row terms (loaded above, latency hidden by the math)
     if (more && tid < BMB) store_terms(nxt);
