@@ -15,28 +15,29 @@
 // atomics from the 8 XCDs cannot stay in their L2s and go out to memory):
 //
 // attn_bwd_kv_kernel -- dK, dV. One workgroup = one chunk of a 128-key KV
-//   tile's partner Q tiles x one KV head; 4 waves own 32 keys each and walk
-//   the chunk's Q tiles (64 rows; transposed tile list) and the query heads
-//   of the GQA group:
-//   S = Q K^T and dP = dO V^T with the wave's K / V rows held in registers as
-//   B operands, so P and dS leave the 32x32 accumulators with keys across
-//   lanes and queries across registers -- exactly the B-operand layout of
-//   dV^T += dO^T P and dK^T += Q^T dS. Q^T and dO^T are staged in LDS
-//   transposed, the 4-row groups of every 16 query rows ordered (0-3, 8-11,
-//   4-7, 12-15) to match the accumulator's row order. dK / dV stay in
-//   registers and are added to the caller's buffers once at the end. KV
-//   tiles with many partners are split into several chunks by the planner
-//   (so the pass has enough workgroups); their chunks store partial sums in
-//   workspace slots and bwd_kv_reduce_kernel adds the slots up in order, so
-//   the result stays deterministic.
+//   tile's partner Q tiles x one KV head; 8 waves = 4 key groups (32 keys)
+//   x 2 row blocks (32 rows of each 64-row Q tile). The K / V tile sits in
+//   LDS for the whole workgroup and the Q / dO rows of each (Q tile, query
+//   head) iteration arrive by direct global -> LDS copies into a double
+//   buffer. S = Q K^T and dP = dO V^T (K / V rows as B operands) leave the
+//   32x32 accumulators with keys across lanes and queries across registers
+//   -- exactly the B-operand layout of dV^T += dO^T P and dK^T += Q^T dS,
+//   whose A operands dO^T, Q^T come from transposing LDS reads. The two row
+//   blocks' dK / dV partial sums are added through LDS at the end and
+//   written once. Two waves per SIMD (each holds only its keys' dK^T / dV^T
+//   accumulators). KV tiles with many partners are split into several
+//   chunks by the planner (so the pass has enough workgroups); their chunks
+//   store partial sums in workspace slots and bwd_kv_reduce_kernel adds the
+//   slots up in order, so the result stays deterministic.
 //
-// attn_bwd_dq_kernel -- dQ. One workgroup = one 64-row Q tile x one query
-//   head; 2 waves own 32 query rows each and walk the KV tiles that meet the
-//   Q tile, in 64-key halves. As in the forward, S^T = K Q^T and
-//   dP^T = V dO^T put one query per lane pair, P^T and dS^T come out in the
-//   B-operand layout of dQ^T += K^T dS^T, with K^T staged key-permuted in
-//   LDS. Each workgroup owns its dQ rows: the result is added once at the
-//   end with plain loads and stores.
+// attn_bwd_dq_kernel -- dQ. One workgroup = one 64-row Q tile x one or two
+//   query heads of a KV head; 2 waves per head own 32 query rows each and
+//   walk the KV tiles that meet the Q tile, in 64-key halves copied straight
+//   into a double-buffered LDS stage shared by the heads. As in the forward,
+//   S^T = K Q^T and dP^T = V dO^T put one query per lane pair, P^T and dS^T
+//   come out in the B-operand layout of dQ^T += K^T dS^T, whose K^T operand
+//   comes from transposing LDS reads. Each workgroup owns its dQ rows: the
+//   result is added once at the end with plain loads and stores.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -154,39 +155,34 @@ struct KvStage {
   static_assert(BYTES % 1024 == 0 || true, "");
 };
 
+constexpr int NTK = 512;    // threads of the KV kernel: 8 waves = 4 key groups x 2 row blocks
+
 template <int D>
-__global__ __launch_bounds__(NT) void attn_bwd_kv_kernel(BwdParams p) {
+__global__ __launch_bounds__(NTK) void attn_bwd_kv_kernel(BwdParams p) {
   using RT = RowTile<D>;
   using KS = KvStage<D>;
+  constexpr int NW = NTK / 64;
+  constexpr int KVT = BNB * RT::ROW;                 // bytes of the K (or V) tile
   constexpr int STAGE = (KS::BYTES + 1023) & ~1023;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * STAGE];
+  constexpr int ST0 = 2 * KVT;                       // first Q / dO stage
+  constexpr int BYTES = ST0 + 2 * STAGE;
+  static_assert(BYTES >= 2 * (BNB * D * 4), "the dK / dV exchange reuses the buffers");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[BYTES];
 
   const int w = blockIdx.x / p.hkv, g = blockIdx.x % p.hkv;
   if (w >= p.n_work) return;
   const WorkItem kt = p.work[w];
   const WorkRange rg = p.range[w];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int k4 = wave & 3, qb = wave >> 2;           // key group (32 keys) and Q row block (32 rows)
 
-  // this wave's keys: local key index wave*32 + l32 within the tile
-  const int my_key = wave * 32 + l32;
+  // this wave's keys: local key index k4*32 + l32 within the tile
+  const int my_key = k4 * 32 + l32;
   const bool key_ok = my_key < kt.n;
   const int kg = kt.global_start + my_key;
   const int64_t kv_base = int64_t(kt.local_start) * p.kv_row_stride + int64_t(g) * D;
 
-  // K / V rows of this lane's key as B operands (8 consecutive d per k-step)
-  bf16x8 kf[D / 16], vf[D / 16];
-  {
-    const int krow = min(my_key, kt.n - 1);
-    const unsigned short *kp = p.k + kv_base + int64_t(krow) * p.kv_row_stride + 8 * hf;
-    const unsigned short *vp = p.v + kv_base + int64_t(krow) * p.kv_row_stride + 8 * hf;
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-      kf[t] = as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + 16 * t));
-      vf[t] = as_bf16x8(*reinterpret_cast<const u32x4 *>(vp + 16 * t));
-    }
-  }
-
-  f32x16 dka[D / 32], dva[D / 32];     // dK^T / dV^T blocks: lane = key, registers = d
+  f32x16 dka[D / 32], dva[D / 32];     // dK^T / dV^T blocks over this wave's rows: lane = key, registers = d
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
     dka[i] = f32x16{};
@@ -194,19 +190,38 @@ __global__ __launch_bounds__(NT) void attn_bwd_kv_kernel(BwdParams p) {
   }
   const float c = p.c;
 
-  // Copy geometry: chunk position P = (i * 4 + wave) * 64 + lane of a tile
-  // (i < LOADS) holds row P / CPR, chunk (P % CPR) ^ sw(row).
-  constexpr int LOADS = BMB * RT::CPR / NT;
+  // The K / V tile (BNB rows) is copied once into LDS; the Q / dO rows of
+  // each iteration into a double-buffered stage. Copy geometry of a tile:
+  // chunk position P = (i * NW + wave) * 64 + lane holds row P / CPR, chunk
+  // (P % CPR) ^ sw(row).
+  {
+    constexpr int KL = BNB * RT::CPR / NTK;
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+      const int P = (i * NW + wave) * 64 + lane;
+      const int row = P / RT::CPR;
+      const int64_t off = kv_base + int64_t(min(row, kt.n - 1)) * p.kv_row_stride + 8 * ((P % RT::CPR) ^ RT::sw(row));
+      const int dst = (i * NW + wave) * 1024;
+      __builtin_amdgcn_global_load_lds((global_void *)(p.k + off), (lds_void *)(lds + dst), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_void *)(p.v + off), (lds_void *)(lds + KVT + dst), 16, 0, 0);
+    }
+  }
+  constexpr int LOADS = BMB * RT::CPR / NTK;
+  static_assert(LOADS >= 1 && LOADS * NTK == BMB * RT::CPR, "Q / dO copies must split evenly");
   int src_row[LOADS], src_col[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int P = (i * 4 + wave) * 64 + lane;
+    const int P = (i * NW + wave) * 64 + lane;
     src_row[i] = P / RT::CPR;
     src_col[i] = 8 * ((P % RT::CPR) ^ RT::sw(P / RT::CPR));
   }
-  // Row-operand reads (A of S = Q K^T, dP = dO V^T): row qb*32 + l32, chunk
-  // 2t + hf; the offset of step t is r_off ^ (32 t).
+  // Row-operand reads: A of S = Q K^T, dP = dO V^T (row qb*32 + l32, chunk
+  // 2t + hf) and B = K / V rows of this wave's keys (row k4*32 + l32); the
+  // swizzle depends on the low 4 row bits only, so both are r_off-based and
+  // the offset of k-step t is off ^ (32 t).
   const int r_off = l32 * RT::ROW + 16 * (hf ^ RT::sw(l32));
+  const int a_off = qb * 32 * RT::ROW + r_off;
+  const int b_off = k4 * 32 * RT::ROW + r_off;
   // Transposing reads (A of dV^T += dO^T P, dK^T += Q^T dS): within each
   // 16-lane group q, lane s addresses row 4 (q / 2) + s / 4 (+ the step's
   // base, a multiple of 8) and columns 16 (q % 2) + 4 (s % 4) .. +3 of the
@@ -223,12 +238,11 @@ __global__ __launch_bounds__(NT) void attn_bwd_kv_kernel(BwdParams p) {
       t_off[db] = row * RT::ROW + 16 * ((col >> 3) ^ RT::sw(row)) + 2 * (col & 7);
     }
   }
-  constexpr int T8 = RT::CPR >= 16 ? 8 * RT::ROW + 0 : 8 * RT::ROW;   // byte distance of the +8-row read
   auto tr_pair = [&](const unsigned char *tile, int base_row, int db) {
     const unsigned char *a = tile + t_off[db] + base_row * RT::ROW;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a));
-    const unsigned char *b2 = RT::CPR >= 16 ? tile + ((t_off[db] ^ 128) + base_row * RT::ROW + T8)
-                                            : a + T8;
+    const unsigned char *b2 = RT::CPR >= 16 ? tile + ((t_off[db] ^ 128) + (base_row + 8) * RT::ROW)
+                                            : a + 8 * RT::ROW;
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(b2));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
@@ -242,8 +256,8 @@ __global__ __launch_bounds__(NT) void attn_bwd_kv_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int64_t off = base + int64_t(min(src_row[i], t.n - 1)) * p.q_row_stride + src_col[i];
-      lds_void *dq = (lds_void *)(stage + KS::Q + (i * 4 + wave) * 1024);
-      lds_void *dd = (lds_void *)(stage + KS::DO + (i * 4 + wave) * 1024);
+      lds_void *dq = (lds_void *)(stage + KS::Q + (i * NW + wave) * 1024);
+      lds_void *dd = (lds_void *)(stage + KS::DO + (i * NW + wave) * 1024);
       __builtin_amdgcn_global_load_lds((global_void *)(p.q + off), dq, 16, 0, 0);
       __builtin_amdgcn_global_load_lds((global_void *)(p.dout + off), dd, 16, 0, 0);
     }
@@ -269,44 +283,38 @@ __global__ __launch_bounds__(NT) void attn_bwd_kv_kernel(BwdParams p) {
     reinterpret_cast<int *>(stage + KS::DS)[tid] = rt_s;
   };
 
-  issue_rows(0, lds);
+  issue_rows(0, lds + ST0);
   if (tid < BMB) {
     load_terms(0);
-    store_terms(lds);
+    store_terms(lds + ST0);
   }
   __syncthreads();
 
   for (int itr = 0; itr < n_iter; ++itr) {
     const PartnerEntry qt = p.partners[rg.begin + itr / p.group];
-    unsigned char *cur = lds + (itr & 1) * STAGE;
-    unsigned char *nxt = lds + ((itr + 1) & 1) * STAGE;
+    unsigned char *cur = lds + ST0 + (itr & 1) * STAGE;
+    unsigned char *nxt = lds + ST0 + ((itr + 1) & 1) * STAGE;
     const bool more = itr + 1 < n_iter;
     if (more) {
       issue_rows(itr + 1, nxt);
       if (tid < BMB) load_terms(itr + 1);
     }
 
-    // ---- S = Q K^T, dP = dO V^T (64 queries x this wave's 32 keys)
-    f32x16 sacc[2], pacc[2];
+    // ---- S = Q K^T, dP = dO V^T (this wave's 32 rows x 32 keys)
+    f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      sacc[qb] = f32x16{};
-      pacc[qb] = f32x16{};
+    for (int t = 0; t < D / 16; ++t) {
+      const bf16x8 aq = as_bf16x8(*reinterpret_cast<const u32x4 *>(cur + KS::Q + (a_off ^ (32 * t))));
+      const bf16x8 ad = as_bf16x8(*reinterpret_cast<const u32x4 *>(cur + KS::DO + (a_off ^ (32 * t))));
+      const bf16x8 bk = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + (b_off ^ (32 * t))));
+      const bf16x8 bv = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + KVT + (b_off ^ (32 * t))));
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bk, sacc, 0, 0, 0);
+      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, bv, pacc, 0, 0, 0);
     }
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int off = qb * 32 * RT::ROW + (r_off ^ (32 * t));
-        const bf16x8 aq = as_bf16x8(*reinterpret_cast<const u32x4 *>(cur + KS::Q + off));
-        const bf16x8 ad = as_bf16x8(*reinterpret_cast<const u32x4 *>(cur + KS::DO + off));
-        sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[t], sacc[qb], 0, 0, 0);
-        pacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[t], pacc[qb], 0, 0, 0);
-      }
 
-    // ---- P and dS; accumulator element i of block qb is query row
+    // ---- P and dS; accumulator element i is query row
     //      qb*32 + 8*(i/4) + 4*hf + (i%4), key my_key. The per-row terms of a
-    //      lane's 16 rows come as four 4-row vector reads per block.
+    //      lane's 16 rows come as four 4-row vector reads.
     const bool masked = qt.cls != SAP_TILE_FULL || qt.n < BMB || kt.n < BNB;
     // a row r sees this lane's key iff r >= rmin (causality; invalid keys see
     // no row) and kg >= ds[r] (document start; INT_MIN unless PARTIAL)
@@ -314,52 +322,49 @@ __global__ __launch_bounds__(NT) void attn_bwd_kv_kernel(BwdParams p) {
     const float *s_lse2 = reinterpret_cast<const float *>(cur + KS::LSE2);
     const float *s_delta = reinterpret_cast<const float *>(cur + KS::DELTA);
     const int *s_ds = reinterpret_cast<const int *>(cur + KS::DS);
-    bf16x8 pb[2][2], sb[2][2];
+    bf16x8 pb[2], sb[2];
     auto p_and_ds = [&](auto mask_tag) {
       constexpr bool MASK = decltype(mask_tag)::value;
+      f32x4 l4[4], d4[4];
+      int ds4[4][4];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x4 l4[4], d4[4];
-        int ds4[4][4];
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int r0 = qb * 32 + 8 * g4 + 4 * hf;
+        l4[g4] = *reinterpret_cast<const f32x4 *>(s_lse2 + r0);
+        d4[g4] = *reinterpret_cast<const f32x4 *>(s_delta + r0);
+        if (MASK) {
+          const u32x4 dsv = *reinterpret_cast<const u32x4 *>(s_ds + r0);
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int r0 = qb * 32 + 8 * g4 + 4 * hf;
-          l4[g4] = *reinterpret_cast<const f32x4 *>(s_lse2 + r0);
-          d4[g4] = *reinterpret_cast<const f32x4 *>(s_delta + r0);
-          if (MASK) {
-            const u32x4 dsv = *reinterpret_cast<const u32x4 *>(s_ds + r0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ds4[g4][e] = int(dsv[e]);
-          }
+          for (int e = 0; e < 4; ++e) ds4[g4][e] = int(dsv[e]);
         }
+      }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          float pv[8], sv[8];
+      for (int u = 0; u < 2; ++u) {
+        float pv[8], sv[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int i = 8 * u + j;
-            const int g4 = i >> 2, e = i & 3;
-            float x = __builtin_fmaf(sacc[qb][i], c, -l4[g4][e]);
-            if (MASK) {          // masked pairs: exp2(-inf) = 0 (a select, not a branch)
-              const int r = qb * 32 + 8 * g4 + 4 * hf + e;
-              x = ((r >= rmin) & (kg >= ds4[g4][e])) ? x : -INFINITY;
-            }
-            const float pr = __builtin_amdgcn_exp2f(x);
-            pv[j] = pr;
-            sv[j] = pr * (pacc[qb][i] - d4[g4][e]);
+        for (int j = 0; j < 8; ++j) {
+          const int i = 8 * u + j;
+          const int g4 = i >> 2, e = i & 3;
+          float x = __builtin_fmaf(sacc[i], c, -l4[g4][e]);
+          if (MASK) {          // masked pairs: exp2(-inf) = 0 (a select, not a branch)
+            const int r = qb * 32 + 8 * g4 + 4 * hf + e;
+            x = ((r >= rmin) & (kg >= ds4[g4][e])) ? x : -INFINITY;
           }
-          u32x4 pk, sk;
-          pk.x = pack_bf16(pv[0], pv[1]);
-          pk.y = pack_bf16(pv[2], pv[3]);
-          pk.z = pack_bf16(pv[4], pv[5]);
-          pk.w = pack_bf16(pv[6], pv[7]);
-          sk.x = pack_bf16(sv[0], sv[1]);
-          sk.y = pack_bf16(sv[2], sv[3]);
-          sk.z = pack_bf16(sv[4], sv[5]);
-          sk.w = pack_bf16(sv[6], sv[7]);
-          pb[qb][u] = as_bf16x8(pk);
-          sb[qb][u] = as_bf16x8(sk);
+          const float pr = __builtin_amdgcn_exp2f(x);
+          pv[j] = pr;
+          sv[j] = pr * (pacc[i] - d4[g4][e]);
         }
+        u32x4 pk, sk;
+        pk.x = pack_bf16(pv[0], pv[1]);
+        pk.y = pack_bf16(pv[2], pv[3]);
+        pk.z = pack_bf16(pv[4], pv[5]);
+        pk.w = pack_bf16(pv[6], pv[7]);
+        sk.x = pack_bf16(sv[0], sv[1]);
+        sk.y = pack_bf16(sv[2], sv[3]);
+        sk.z = pack_bf16(sv[4], sv[5]);
+        sk.w = pack_bf16(sv[6], sv[7]);
+        pb[u] = as_bf16x8(pk);
+        sb[u] = as_bf16x8(sk);
       }
     };
     if (masked)
@@ -368,24 +373,58 @@ __global__ __launch_bounds__(NT) void attn_bwd_kv_kernel(BwdParams p) {
       p_and_ds(std::false_type{});
 
     // ---- dV^T += dO^T P, dK^T += Q^T dS (k = 16 query rows per step; the
-    //      rows of k-step (qb, u) are qb*32 + 16u + 4hf + (0..3 | 8..11))
+    //      rows of step u are qb*32 + 16u + 4hf + (0..3 | 8..11))
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 ado = tr_pair(cur + KS::DO, qb * 32 + 16 * u, db);
-          const bf16x8 aqt = tr_pair(cur + KS::Q, qb * 32 + 16 * u, db);
-          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, pb[qb][u], dva[db], 0, 0, 0);
-          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, sb[qb][u], dka[db], 0, 0, 0);
-        }
+      for (int db = 0; db < D / 32; ++db) {
+        const bf16x8 ado = tr_pair(cur + KS::DO, qb * 32 + 16 * u, db);
+        const bf16x8 aqt = tr_pair(cur + KS::Q, qb * 32 + 16 * u, db);
+        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, pb[u], dva[db], 0, 0, 0);
+        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, sb[u], dka[db], 0, 0, 0);
+      }
 
     // the next iteration's row terms (loaded above, latency hidden by the math)
     if (more && tid < BMB) store_terms(nxt);
     // copies for the next iteration have landed and every wave is done with this stage
     __syncthreads();
   }
+
+  // ---- the two row blocks' partial sums meet in LDS: row block 1 stores its
+  //      registers lane-minor ([k4][register quad][lane] float4s), row block 0
+  //      adds them
+  f32x4 *xk = reinterpret_cast<f32x4 *>(lds);
+  f32x4 *xv = xk + 4 * (D / 8) * 64;
+  if (qb == 1) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) {
+        const int idx = (k4 * (D / 8) + db * 4 + ig) * 64 + lane;
+        f32x4 a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = dka[db][4 * ig + e];
+          b[e] = dva[db][4 * ig + e];
+        }
+        xk[idx] = a;
+        xv[idx] = b;
+      }
+  }
+  __syncthreads();
+  if (qb == 1) return;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int ig = 0; ig < 4; ++ig) {
+      const int idx = (k4 * (D / 8) + db * 4 + ig) * 64 + lane;
+      const f32x4 a = xk[idx], b = xv[idx];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dka[db][4 * ig + e] += a[e];
+        dva[db][4 * ig + e] += b[e];
+      }
+    }
 
   if (!key_ok) return;
   const int slot = p.slot[w];
@@ -702,9 +741,9 @@ hipError_t launch_attn_bwd(const BwdLaunch &a, hipStream_t stream) {
     p.n_work = a.n_work;
     const dim3 grid{static_cast<unsigned>(a.n_work * a.hkv)};
     if (a.d == 128)
-      hipLaunchKernelGGL(attn_bwd_kv_kernel<128>, grid, dim3(NT), 0, stream, p);
+      hipLaunchKernelGGL(attn_bwd_kv_kernel<128>, grid, dim3(NTK), 0, stream, p);
     else
-      hipLaunchKernelGGL(attn_bwd_kv_kernel<64>, grid, dim3(NT), 0, stream, p);
+      hipLaunchKernelGGL(attn_bwd_kv_kernel<64>, grid, dim3(NTK), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.n_reduce > 0) {
