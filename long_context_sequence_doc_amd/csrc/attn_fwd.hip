@@ -8,8 +8,10 @@
 // natural-log log-sum-exp so partial results over disjoint KV sets merge
 // exactly.
 //
-// Layout of the work (one workgroup = one Q tile x one query head):
-//   * 4 waves, each owns 32 query rows of the 128-row tile.
+// Layout of the work (one workgroup = one 128-row Q tile x NH query heads of
+// one KV head; NH = 2 when the GQA group size is even, else 1):
+//   * 4 waves per head, each owns 32 query rows of the tile; the heads'
+//     waves share every staged K / V tile.
 //   * Per 64-key KV tile: S^T = K Q^T with v_mfma_f32_32x32x16_bf16. In the
 //     32x32 accumulator a lane holds one column (= one query) and 16 rows (=
 //     keys), so a query's scores sit in one lane pair (lane, lane ^ 32): row
@@ -58,7 +60,7 @@ typedef __attribute__((address_space(1))) void global_void;
 
 constexpr int BM = 128;
 constexpr int BN = 64;
-constexpr int NWAVES = 4;
+constexpr int NWAVES = 4;                 // waves per query head
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int NXCD = 8;
 constexpr float LOG2E = 1.4426950408889634f;
@@ -83,14 +85,14 @@ struct FwdParams {
 // LDS geometry of one stage: K tile then V tile, each BN rows x D bf16,
 // row-major, unpadded; 16-byte chunk j of row r is stored at chunk position
 // j ^ ksw(r) (K) or j ^ vsw(r) (V).
-template <int D>
+template <int D, int NT>
 struct Stage {
   static constexpr int CPR = D / 8;                    // 16-byte chunks per row
   static constexpr int ROW = 2 * D;                    // bytes per row
   static constexpr int TILE = BN * ROW;                // bytes of the K (or V) tile
   static constexpr int BYTES = 2 * TILE;
-  static constexpr int LOADS = BN * CPR / NTHREADS;    // 16-byte loads per thread per tile
-  static_assert(LOADS * NTHREADS == BN * CPR, "the tile must split evenly over the threads");
+  static constexpr int LOADS = BN * CPR / NT;          // 16-byte loads per thread per tile
+  static_assert(LOADS * NT == BN * CPR, "the tile must split evenly over the threads");
   // K is read as 16-byte row chunks by 32 consecutive rows: chunk ^ (row % CPR)
   // spreads any run of CPR consecutive rows over distinct chunk positions.
   static __device__ int ksw(int row) { return row % CPR; }
@@ -102,22 +104,23 @@ struct Stage {
 
 // Per-thread element offsets (from the tile's first row of the KV head) of
 // the global chunks this thread copies into LDS. Chunk position P of a tile
-// (16 bytes each, in LDS order) is written by load i = P / NTHREADS of wave
-// (P / 64) % NWAVES, lane P % 64. Rows past a short tile's end repeat its last
+// (16 bytes each, in LDS order) is written by load i = P / NT of wave
+// (P / 64) % (NT / 64), lane P % 64, for a workgroup of NT threads. Rows past
+// a short tile's end repeat its last
 // row (finite values; their scores are masked to -inf, their P is 0).
-template <int D>
+template <int D, int NT>
 struct LoadOffsets {
-  int k[Stage<D>::LOADS];
-  int v[Stage<D>::LOADS];
+  int k[Stage<D, NT>::LOADS];
+  int v[Stage<D, NT>::LOADS];
 };
 
-template <int D>
-__device__ inline LoadOffsets<D> load_offsets(int stride, int wave, int lane, int rows) {
-  using G = Stage<D>;
-  LoadOffsets<D> o;
+template <int D, int NT>
+__device__ inline LoadOffsets<D, NT> load_offsets(int stride, int wave, int lane, int rows) {
+  using G = Stage<D, NT>;
+  LoadOffsets<D, NT> o;
 #pragma unroll
   for (int i = 0; i < G::LOADS; ++i) {
-    const int P = (i * NWAVES + wave) * 64 + lane;
+    const int P = (i * (NT / 64) + wave) * 64 + lane;
     const int row = P / G::CPR, pos = P % G::CPR;
     const int src = min(row, rows - 1) * stride;
     o.k[i] = src + 8 * (pos ^ G::ksw(row));
@@ -127,22 +130,22 @@ __device__ inline LoadOffsets<D> load_offsets(int stride, int wave, int lane, in
 }
 
 // Issues the direct global -> LDS copies of one KV tile into a stage.
-template <int D>
+template <int D, int NT>
 __device__ inline void issue_tile(const FwdParams &p, const PartnerEntry &pe, int g, unsigned char *stage,
-                                  int wave, int lane, const LoadOffsets<D> &full) {
-  using G = Stage<D>;
+                                  int wave, int lane, const LoadOffsets<D, NT> &full) {
+  using G = Stage<D, NT>;
   const int64_t base = int64_t(pe.local_start) * p.kv_row_stride + int64_t(g) * D;
   const unsigned short *kb = p.k + base;
   const unsigned short *vb = p.v + base;
-  const LoadOffsets<D> o = pe.n == BN ? full : load_offsets<D>(int(p.kv_row_stride), wave, lane, pe.n);
+  const LoadOffsets<D, NT> o = pe.n == BN ? full : load_offsets<D, NT>(int(p.kv_row_stride), wave, lane, pe.n);
 #pragma unroll
   for (int i = 0; i < G::LOADS; ++i)
     __builtin_amdgcn_global_load_lds((global_void *)(kb + o.k[i]),
-                                     (lds_void *)(stage + (i * NWAVES + wave) * 1024), 16, 0, 0);
+                                     (lds_void *)(stage + (i * (NT / 64) + wave) * 1024), 16, 0, 0);
 #pragma unroll
   for (int i = 0; i < G::LOADS; ++i)
     __builtin_amdgcn_global_load_lds((global_void *)(vb + o.v[i]),
-                                     (lds_void *)(stage + G::TILE + (i * NWAVES + wave) * 1024), 16, 0, 0);
+                                     (lds_void *)(stage + G::TILE + (i * (NT / 64) + wave) * 1024), 16, 0, 0);
 }
 
 __device__ inline bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -159,25 +162,27 @@ __device__ inline unsigned pack_bf16(float lo, float hi) {
 // MERGE: o / lse hold a running result that this call's partial is merged
 // into (the ring step's merge folded into the epilogue), instead of being
 // overwritten.
-template <int D, bool MERGE>
-__global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(FwdParams p) {
-  using ST = Stage<D>;
+template <int D, bool MERGE, int NH>
+__global__ __launch_bounds__(NTHREADS * NH) void attn_fwd_kernel(FwdParams p) {
+  constexpr int NT = NTHREADS * NH;
+  using ST = Stage<D, NT>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * ST::BYTES];
 
   // workgroup -> (work item, query head), XCD-aware
   const int b = blockIdx.x;
   const int xcd = b % NXCD, slot = b / NXCD;
-  const int G = (slot / p.group) * NXCD + xcd;
+  const int pairs = p.group / NH;
+  const int G = (slot / pairs) * NXCD + xcd;
   if (G >= p.n_groups) return;
   const int w = G / p.hkv, g = G % p.hkv;
-  const int h = g * p.group + slot % p.group;
+  const int h = g * p.group + (slot % pairs) * NH + (threadIdx.x >> 8);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const WorkItem wi = p.work[w];
   const WorkRange rg = p.range[w];
 
-  const int my_row = wave * 32 + l32;             // row within the Q tile
+  const int my_row = (wave & 3) * 32 + l32;       // row within the Q tile
   const bool row_ok = my_row < wi.n;
   const int qg = wi.global_start + my_row;        // global position of this lane's query
   const int dsq = row_ok ? p.ds_q[wi.local_start + my_row] : 0;
@@ -198,7 +203,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(FwdParams p) {
   float l_part = 0.f;         // this lane's share of the softmax denominator
   const float c = p.c;
 
-  const LoadOffsets<D> full_offs = load_offsets<D>(int(p.kv_row_stride), wave, lane, BN);
+  const LoadOffsets<D, NT> full_offs = load_offsets<D, NT>(int(p.kv_row_stride), wave, lane, BN);
 
   // LDS byte offsets (within a stage) of this lane's operand reads.
   // K (A operand of S^T): row l32 (+32 for the second key block), chunk
@@ -222,7 +227,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(FwdParams p) {
   }
   const PartnerEntry *pes = p.partners + rg.begin;
   PartnerEntry pe = pes[0];
-  issue_tile<D>(p, pe, g, lds, wave, lane, full_offs);
+  issue_tile<D, NT>(p, pe, g, lds, wave, lane, full_offs);
   __syncthreads();
 
   for (int it = 0; it < rg.count; ++it) {
@@ -231,7 +236,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(FwdParams p) {
     const bool more = it + 1 < rg.count;
     if (more) {
       pe = pes[it + 1];
-      issue_tile<D>(p, pe, g, lds + ((it + 1) & 1) * ST::BYTES, wave, lane, full_offs);
+      issue_tile<D, NT>(p, pe, g, lds + ((it + 1) & 1) * ST::BYTES, wave, lane, full_offs);
     }
 
     // S^T for 64 keys x this wave's 32 queries: two independent accumulator
@@ -392,22 +397,21 @@ hipError_t launch_attn_fwd(const FwdLaunch &a, hipStream_t stream) {
   p.n_groups = a.n_work * a.hkv;
   p.scale = a.scale;
   p.c = a.scale * LOG2E;
+  const int nh = p.group % 2 == 0 ? 2 : 1;         // query heads per workgroup
   const int64_t slots = (int64_t(p.n_groups) + NXCD - 1) / NXCD;
-  const int64_t blocks = slots * NXCD * p.group;
+  const int64_t blocks = slots * NXCD * (p.group / nh);
   // 32-bit row offsets inside a 64-row tile
   if (blocks > INT32_MAX || a.kv_row_stride > INT32_MAX / BN) return hipErrorInvalidValue;
-  const dim3 grid{static_cast<unsigned>(blocks)}, block{NTHREADS};
+  const dim3 grid{static_cast<unsigned>(blocks)}, block{static_cast<unsigned>(NTHREADS * nh)};
+#define SAP_FWD_LAUNCH(DD, MM, HH) hipLaunchKernelGGL((attn_fwd_kernel<DD, MM, HH>), grid, block, 0, stream, p)
   if (a.d == 128) {
-    if (a.merge)
-      hipLaunchKernelGGL((attn_fwd_kernel<128, true>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((attn_fwd_kernel<128, false>), grid, block, 0, stream, p);
+    if (nh == 2) { if (a.merge) SAP_FWD_LAUNCH(128, true, 2); else SAP_FWD_LAUNCH(128, false, 2); }
+    else { if (a.merge) SAP_FWD_LAUNCH(128, true, 1); else SAP_FWD_LAUNCH(128, false, 1); }
   } else {
-    if (a.merge)
-      hipLaunchKernelGGL((attn_fwd_kernel<64, true>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((attn_fwd_kernel<64, false>), grid, block, 0, stream, p);
+    if (nh == 2) { if (a.merge) SAP_FWD_LAUNCH(64, true, 2); else SAP_FWD_LAUNCH(64, false, 2); }
+    else { if (a.merge) SAP_FWD_LAUNCH(64, true, 1); else SAP_FWD_LAUNCH(64, false, 1); }
   }
+#undef SAP_FWD_LAUNCH
   return hipGetLastError();
 }
 
