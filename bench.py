@@ -304,6 +304,30 @@ def main():
         "kernels": kernels,
     }
     if len(rf.active) > 1 and not headline_bwd:
+        # the same forward as one call over all steps' KV (a rank holding every chunk)
+        rc = RankForward.concatenated(w.cu, w.q_segs, kv_steps, w.hq, w.hkv, w.d, w.scale)
+        rc_plan = rc.plans[0]
+
+        def one_call(tm):
+            tm.run("attn_fwd", lambda: sap.sap_attn_fwd(rc_plan, q, k, v, qs, ks, w.hq, w.hkv, w.d, w.scale,
+                                                        rc.o, rc.lse))
+        warm = _Timer(stream)
+        for _ in range(a.warmup):
+            one_call(warm)
+        torch.cuda.synchronize()
+        tm_c = _Timer(stream)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(a.steps):
+            one_call(tm_c)
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms_c = start.elapsed_time(end) / a.steps
+        line["forward_single_call"] = {
+            "step": "forward as one call over every step's KV segments (all chunks resident; no merge)",
+            "value": round(fwd_flop / (ms_c * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "ms_per_step": round(ms_c, 4),
+            "kernels": {"attn_fwd": kernel_stats(tm_c, "attn_fwd", fwd_flop)}}
+        rc.close()
         # reference: the same forward with a separate merge pass per step
         tm_2, ms_2 = timed(False, fused=False)
         _, value_2, kernels_2 = report(tm_2, ms_2, False)

@@ -20,7 +20,9 @@ one rank's work is:
     document masks most remote chunks of a rank hold no key its rows may see.
 
 A head-sharded (Ulysses) rank is the one-step case with Q = KV = the whole
-sequence for its heads.
+sequence for its heads. A rank that already holds every step's KV can also
+run all steps as one call: ``concatenated(...)`` builds one plan over the
+union of the steps' KV segments (one launch, no merge at all).
 
 The backward (RankBackward) runs the recompute-based backward once per
 non-empty step with the final O and LSE; the per-step dQ / dK / dV add up to
@@ -102,6 +104,15 @@ class RankForward:
         for p in self.plans:
             sap_plan_free(p)
         self.plans = []
+
+    @classmethod
+    def concatenated(cls, cu_seqlens, q_segs, step_kv_segs, hq: int, hkv: int, d: int, scale: float,
+                     device: str = "cuda"):
+        """One forward call over every step's KV segments together (the steps
+        must address disjoint KV rows): the fused ring pass for a rank whose KV
+        chunks are all resident."""
+        union = [seg for segs in step_kv_segs for seg in segs]
+        return cls(cu_seqlens, q_segs, [union], hq, hkv, d, scale, device)
 
 
 class RankBackward:

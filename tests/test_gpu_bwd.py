@@ -53,16 +53,17 @@ def _bwd_call(sap, cu, q_segs, kv_segs, qd, kd, vd, dod, o, lse, hq, hkv, d, sca
     return plan, ws          # the caller keeps both alive until the stream is synchronised
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(10))
 def test_random_small_layouts(seed):
-    """Ragged tiles, 1-token and empty documents, GQA, D in {64, 128}, a
+    """Ragged tiles, 1-token and empty documents, GQA (group sizes 1-4; odd
+    and even groups take different workgroup shapes), D in {64, 128}, a
     sharded Q (two segments, local != global rows) and KV in two pieces."""
     sap = _sap()
     import torch
     rng = np.random.default_rng(700 + seed)
     d = 128 if seed % 2 else 64
     hkv = int(rng.choice([1, 2]))
-    hq = hkv * int(rng.choice([1, 2, 4]))
+    hq = hkv * (int(rng.choice([1, 2, 4])) if seed < 8 else 3)
     total = int(rng.integers(200, 900))
     lengths = W.random_docs(rng, total, int(rng.integers(2, 400)))
     cu = W.cu_seqlens(lengths)

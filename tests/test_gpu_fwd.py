@@ -176,6 +176,26 @@ def test_ring_rank_fused_merge():
     rf.close()
 
 
+def test_ring_rank_single_call():
+    """32K ring, rank 3, every step's KV in one plan and one call (no merge):
+    all rows against the oracle."""
+    _sap()
+    import torch
+    from long_context_sequence_doc_amd.rank import RankForward
+    say("case ring_sp8_32k_rank3: one call over all steps' KV")
+    w = W.by_name("ring")
+    t = tensors("ring")
+    rc = RankForward.concatenated(w.cu, w.q_segs, [s.kv_segs for s in w.steps], w.hq, w.hkv, w.d, w.scale)
+    q = to_dev(W.local_rows(t.q, w.q_segs))
+    k, v = to_dev(t.k), to_dev(t.v)
+    rc.run(q, k, v, q.stride(0), k.stride(0))
+    torch.cuda.synchronize()
+    gq = w.q_global_rows()
+    ro, rl = A.forward(f64(W.local_rows(t.q, w.q_segs)), f64(t.k), f64(t.v), gq, np.arange(w.total), w.cu, w.scale)
+    compare(rc.o.cpu().numpy(), rc.lse.cpu().numpy(), ro, rl, label="ring single call")
+    rc.close()
+
+
 @pytest.mark.parametrize("seed", range(4))
 def test_fused_merge_random(seed):
     """sap_attn_fwd over KV part A, then sap_attn_fwd_merge over part B, against
