@@ -302,14 +302,22 @@ __global__ __launch_bounds__(NTK) void attn_bwd_kv_kernel(BwdParams p) {
 
     // ---- S = Q K^T, dP = dO V^T (this wave's 32 rows x 32 keys)
     f32x16 sacc = f32x16{}, pacc = f32x16{};
+    {
+      auto rd = [&](const unsigned char *base, int off) { return as_bf16x8(*reinterpret_cast<const u32x4 *>(base + off)); };
+      bf16x8 aq = rd(cur + KS::Q, a_off), ad = rd(cur + KS::DO, a_off), bk = rd(lds, b_off), bv = rd(lds + KVT, b_off);
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-      const bf16x8 aq = as_bf16x8(*reinterpret_cast<const u32x4 *>(cur + KS::Q + (a_off ^ (32 * t))));
-      const bf16x8 ad = as_bf16x8(*reinterpret_cast<const u32x4 *>(cur + KS::DO + (a_off ^ (32 * t))));
-      const bf16x8 bk = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + (b_off ^ (32 * t))));
-      const bf16x8 bv = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + KVT + (b_off ^ (32 * t))));
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bk, sacc, 0, 0, 0);
-      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, bv, pacc, 0, 0, 0);
+      for (int t = 0; t < D / 16; ++t) {
+        bf16x8 naq = aq, nad = ad, nbk = bk, nbv = bv;
+        if (t + 1 < D / 16) {
+          naq = rd(cur + KS::Q, a_off ^ (32 * (t + 1)));
+          nad = rd(cur + KS::DO, a_off ^ (32 * (t + 1)));
+          nbk = rd(lds, b_off ^ (32 * (t + 1)));
+          nbv = rd(lds + KVT, b_off ^ (32 * (t + 1)));
+        }
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bk, sacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, bv, pacc, 0, 0, 0);
+        aq = naq; ad = nad; bk = nbk; bv = nbv;
+      }
     }
 
     // ---- P and dS; accumulator element i is query row
@@ -374,15 +382,23 @@ __global__ __launch_bounds__(NTK) void attn_bwd_kv_kernel(BwdParams p) {
 
     // ---- dV^T += dO^T P, dK^T += Q^T dS (k = 16 query rows per step; the
     //      rows of step u are qb*32 + 16u + 4hf + (0..3 | 8..11))
+    {
+      bf16x8 ado = tr_pair(cur + KS::DO, qb * 32, 0), aqt = tr_pair(cur + KS::Q, qb * 32, 0);
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const bf16x8 ado = tr_pair(cur + KS::DO, qb * 32 + 16 * u, db);
-        const bf16x8 aqt = tr_pair(cur + KS::Q, qb * 32 + 16 * u, db);
+      for (int k = 0; k < 2 * (D / 32); ++k) {
+        const int u = k / (D / 32), db = k % (D / 32);
+        bf16x8 n_do = ado, n_qt = aqt;
+        if (k + 1 < 2 * (D / 32)) {
+          const int u1 = (k + 1) / (D / 32), db1 = (k + 1) % (D / 32);
+          n_do = tr_pair(cur + KS::DO, qb * 32 + 16 * u1, db1);
+          n_qt = tr_pair(cur + KS::Q, qb * 32 + 16 * u1, db1);
+        }
         dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, pb[u], dva[db], 0, 0, 0);
         dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, sb[u], dka[db], 0, 0, 0);
+        ado = n_do;
+        aqt = n_qt;
       }
+    }
 
     // the next iteration's row terms (loaded above, latency hidden by the math)
     if (more && tid < BMB) store_terms(nxt);
