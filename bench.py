@@ -334,6 +334,37 @@ def main():
         line["forward_two_pass"] = {"step": "forward (ring steps + separate lse_merge pass per step)",
                                     "value": round(value_2, 3), "unit": "TFLOP/s", "ms_per_step": round(ms_2, 4),
                                     "kernels": kernels_2}
+    if with_bwd and not headline_bwd and len(rf.active) > 1:
+        # the same training step as one forward call and one backward call over
+        # every step's KV (a rank holding every chunk)
+        rc = RankForward.concatenated(w.cu, w.q_segs, kv_steps, w.hq, w.hkv, w.d, w.scale)
+        rbc = RankBackward.concatenated(w.cu, w.q_segs, kv_steps, w.hq, w.hkv, w.d, w.scale)
+
+        def one_train(tm):
+            tm.run("attn_fwd", lambda: sap.sap_attn_fwd(rc.plans[0], q, k, v, qs, ks, w.hq, w.hkv, w.d, w.scale,
+                                                        rc.o, rc.lse))
+            tm.run("bwd_rowterm", lambda: rbc.rowterm(rc.o, dout, qs))
+            tm.run("attn_bwd", lambda: rbc.accumulate(0, q, k, v, rc.lse, dout, qs, ks, dq, dk, dv))
+        warm = _Timer(stream)
+        for _ in range(a.warmup):
+            one_train(warm)
+        torch.cuda.synchronize()
+        tm_c = _Timer(stream)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(a.steps):
+            one_train(tm_c)
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms_c = start.elapsed_time(end) / a.steps
+        line["training_step_single_call"] = {
+            "step": "forward + backward as one call each over every step's KV segments (all chunks resident)",
+            "value": round((fwd_flop + bwd_flop) / (ms_c * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+            "ms_per_step": round(ms_c, 4),
+            "kernels": {"attn_fwd": kernel_stats(tm_c, "attn_fwd", fwd_flop),
+                        "attn_bwd": kernel_stats(tm_c, "attn_bwd", bwd_flop)}}
+        rc.close()
+        rbc.close()
     if with_bwd and not headline_bwd:
         # the same shard's training step: forward + recompute backward
         tm_t, ms_t = timed(True)

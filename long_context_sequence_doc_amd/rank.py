@@ -171,3 +171,12 @@ class RankBackward:
         for p in self.plans:
             sap_plan_free(p)
         self.plans = []
+
+    @classmethod
+    def concatenated(cls, cu_seqlens, q_segs, step_kv_segs, hq: int, hkv: int, d: int, scale: float,
+                     device: str = "cuda"):
+        """The backward of every step's KV segments as one call (the steps must
+        address disjoint KV rows): one dK/dV pass and one dQ pass for a rank
+        whose KV chunks are all resident."""
+        union = [seg for segs in step_kv_segs for seg in segs]
+        return cls(cu_seqlens, q_segs, [union], hq, hkv, d, scale, device)

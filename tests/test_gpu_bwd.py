@@ -142,6 +142,16 @@ def test_ring_steps_accumulate_to_full_gradient():
     _check("dQ ring", dq.cpu().numpy(), dq_ref)
     _check("dK ring", dk.cpu().numpy(), dk_ref)
     _check("dV ring", dv.cpu().numpy(), dv_ref)
+    # the same three chunks as one plan and one call
+    say("case bwd ring: the 3 KV chunks in one call")
+    dq.zero_(); dk.zero_(); dv.zero_()
+    keep = _bwd_call(sap, cu, q_segs, [(256 * c, 256 * (c + 1), 256 * c) for c in range(3)], qd, kd, vd, dod, o,
+                     lse, hq, hkv, d, scale, dq, dk, dv)
+    torch.cuda.synchronize()
+    del keep
+    _check("dQ one call", dq.cpu().numpy(), dq_ref)
+    _check("dK one call", dk.cpu().numpy(), dk_ref)
+    _check("dV one call", dv.cpu().numpy(), dv_ref)
 
 
 def test_training_fwd_bwd_sampled():
