@@ -32,8 +32,9 @@
 //
 // attn_bwd_dq_kernel -- dQ. One workgroup = one 64-row Q tile x one or two
 //   query heads of a KV head; 2 waves per head own 32 query rows each and
-//   walk the KV tiles that meet the Q tile, in 64-key halves copied straight
-//   into a double-buffered LDS stage shared by the heads. As in the forward,
+//   walk the KV tiles that meet the Q tile, in 64-key (or, with one head,
+//   32-key) parts copied straight into a double-buffered LDS stage shared by
+//   the heads. As in the forward,
 //   S^T = K Q^T and dP^T = V dO^T put one query per lane pair, P^T and dS^T
 //   come out in the B-operand layout of dQ^T += K^T dS^T, whose K^T operand
 //   comes from transposing LDS reads. Each workgroup owns its dQ rows: the
@@ -521,8 +522,9 @@ constexpr int HK = 64;      // keys per half of a KV tile in the dQ kernel
 
 // dQ kernel: one workgroup = one 64-row Q tile x NH query heads of one KV
 // head (NH = 2 when the GQA group has an even size, so four waves share each
-// staged K / V half-tile). Wave w owns head hq0 + w / 2, rows 32 (w % 2) ..
-// +31. Per 64-key half of a partner KV tile, staged by direct copies into a
+// staged K / V part-tile). Wave w owns head hq0 + w / 2, rows 32 (w % 2) ..
+// +31. Per part of a partner KV tile (64 keys with two heads; 32 with one,
+// so four 2-wave workgroups fit a CU), staged by direct copies into a
 // double-buffered LDS stage (K rows, V rows; swizzled as RowTile):
 //   S^T = K Q^T, dP^T = V dO^T            (A: K / V rows, B: Q / dO in registers)
 //   dS^T = P^T o (dP^T - D)               (one query per lane pair: LSE, D scalars)
@@ -532,9 +534,12 @@ __global__ __launch_bounds__(128 * NH) void attn_bwd_dq_kernel(BwdParams p) {
   using RT = RowTile<D>;
   constexpr int NTD = 128 * NH;                      // threads
   constexpr int NWV = 2 * NH;                        // waves
-  constexpr int KOFF = 0, VOFF = RT::BYTES;          // K, V half-tiles (HK == BMB rows)
-  constexpr int STAGE = 2 * RT::BYTES;
-  static_assert(HK == BMB, "the K / V half-tiles reuse the 64-row tile geometry");
+  // keys per stage: 64 (half a KV tile) with two heads per workgroup; 32 (a
+  // quarter) with one, so that four 2-wave workgroups fit a CU's LDS
+  constexpr int HKQ = NH == 2 ? HK : HK / 2;
+  constexpr int KBQ = HKQ / 32;                      // 32-key blocks per stage
+  constexpr int KOFF = 0, VOFF = HKQ * RT::ROW;      // K, V part-tiles (RowTile rows)
+  constexpr int STAGE = 2 * HKQ * RT::ROW;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * STAGE];
 
   // workgroup -> (Q tile, head pair); the head pairs of one KV head and
@@ -579,8 +584,8 @@ __global__ __launch_bounds__(128 * NH) void attn_bwd_dq_kernel(BwdParams p) {
 
   // copy geometry of a half-tile (see RowTile): chunk position
   // P = (i * NWV + wave) * 64 + lane holds row P / CPR, chunk (P % CPR) ^ sw(row)
-  constexpr int LOADS = HK * RT::CPR / NTD;
-  static_assert(LOADS * NTD == HK * RT::CPR, "copies must split evenly");
+  constexpr int LOADS = HKQ * RT::CPR / NTD;
+  static_assert(LOADS * NTD == HKQ * RT::CPR, "copies must split evenly");
   int src_row[LOADS], src_col[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
@@ -600,8 +605,8 @@ __global__ __launch_bounds__(128 * NH) void attn_bwd_dq_kernel(BwdParams p) {
     }
   }
   auto issue_half = [&](const PartnerEntry &kt, int half, unsigned char *stage) {
-    const int kn = min(HK, kt.n - half * HK);
-    const int64_t base = int64_t(kt.local_start + half * HK) * p.kv_row_stride + int64_t(g) * D;
+    const int kn = min(HKQ, kt.n - half * HKQ);
+    const int64_t base = int64_t(kt.local_start + half * HKQ) * p.kv_row_stride + int64_t(g) * D;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int64_t off = base + int64_t(min(src_row[i], kn - 1)) * p.kv_row_stride + src_col[i];
@@ -620,21 +625,23 @@ __global__ __launch_bounds__(128 * NH) void attn_bwd_dq_kernel(BwdParams p) {
     unsigned char *cur = lds + stage_i * STAGE;
     // the next half: this tile's second one, or the next tile's first
     int nit = it, nhalf = half + 1;
-    if (nhalf * HK >= kt.n) {
+    if (nhalf * HKQ >= kt.n) {
       nit = it + 1;
       nhalf = 0;
     }
     if (nit < rg.count) issue_half(p.partners[rg.begin + nit], nhalf, lds + (stage_i ^ 1) * STAGE);
 
-    const int k0 = half * HK;                     // first key of this half within the tile
-    const int kn = min(HK, kt.n - k0);            // keys in this half
+    const int k0 = half * HKQ;                    // first key of this part within the tile
+    const int kn = min(HKQ, kt.n - k0);           // keys in this part
 
     // ---- S^T = K Q^T, dP^T = V dO^T (64 keys x this wave's 32 queries)
-    f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
+    f32x16 sacc[KBQ], pacc[KBQ];
+#pragma unroll
+    for (int kb = 0; kb < KBQ; ++kb) sacc[kb] = pacc[kb] = f32x16{};
 #pragma unroll
     for (int t = 0; t < D / 16; ++t)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KBQ; ++kb) {
         const int off = kb * 32 * RT::ROW + (r_off ^ (32 * t));
         const bf16x8 ak = as_bf16x8(*reinterpret_cast<const u32x4 *>(cur + KOFF + off));
         const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(cur + VOFF + off));
@@ -644,16 +651,16 @@ __global__ __launch_bounds__(128 * NH) void attn_bwd_dq_kernel(BwdParams p) {
 
     // ---- dS^T = P^T o (dP^T - D); element i of key block kb is key
     //      k0 + kb*32 + 8*(i/4) + 4*hf + (i%4) of the tile
-    const bool masked = kt.cls != SAP_TILE_FULL || kn < HK || qt.n < BMB;
+    const bool masked = kt.cls != SAP_TILE_FULL || kn < HKQ || qt.n < BMB;
     int lo = -(1 << 30), hi = kn - 1;             // allowed half-local key range of this query
     if (masked) {
       if (kt.cls != SAP_TILE_FULL) hi = min(hi, qg - (kt.global_start + k0));
       if (kt.cls == SAP_TILE_PARTIAL) lo = dsq - (kt.global_start + k0);
     }
     const int hi_r = hi - 4 * hf, lo_r = lo - 4 * hf;
-    bf16x8 sb[2][2];
+    bf16x8 sb[KBQ][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KBQ; ++kb)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         float sv[8];
@@ -676,7 +683,7 @@ __global__ __launch_bounds__(128 * NH) void attn_bwd_dq_kernel(BwdParams p) {
 
     // ---- dQ^T += K^T dS^T (k = 16 keys per step: kb*32 + 16u + 4hf + (0..3 | 8..11))
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KBQ; ++kb)
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
