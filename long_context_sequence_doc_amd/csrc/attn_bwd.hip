@@ -74,19 +74,6 @@ __device__ inline unsigned pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-__device__ inline int perm16(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
-
-// Four rows' 16-byte chunks (8 columns each) -> for each column j, the four
-// rows' elements packed as two dwords (rows 0,1 | rows 2,3).
-__device__ inline u32x2 gather4(const u32x4 (&r)[4], int j) {
-  const int w = j >> 1;
-  const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
-  u32x2 pk;
-  pk.x = __builtin_amdgcn_perm(r[1][w], r[0][w], sel);
-  pk.y = __builtin_amdgcn_perm(r[3][w], r[2][w], sel);
-  return pk;
-}
-
 // ---------------------------------------------------------------------------
 // D_r = sum_d dO[r,h,d] * O[r,h,d] for the rows of the plan's Q tiles.
 // 32 threads per (row, head); D/32 elements each.
@@ -153,7 +140,6 @@ struct KvStage {
   static constexpr int DELTA = LSE2 + 4 * BMB;       // float[BMB]
   static constexpr int DS = DELTA + 4 * BMB;         // int[BMB]: document start (INT_MIN unless PARTIAL)
   static constexpr int BYTES = DS + 4 * BMB;
-  static_assert(BYTES % 1024 == 0 || true, "");
 };
 
 constexpr int NTK = 512;    // threads of the KV kernel: 8 waves = 4 key groups x 2 row blocks

@@ -52,7 +52,6 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
-typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -106,8 +105,8 @@ struct Stage {
 // the global chunks this thread copies into LDS. Chunk position P of a tile
 // (16 bytes each, in LDS order) is written by load i = P / NT of wave
 // (P / 64) % (NT / 64), lane P % 64, for a workgroup of NT threads. Rows past
-// a short tile's end repeat its last
-// row (finite values; their scores are masked to -inf, their P is 0).
+// a short tile's end repeat its last row (finite values; their scores are
+// masked to -inf, their P is 0).
 template <int D, int NT>
 struct LoadOffsets {
   int k[Stage<D, NT>::LOADS];
