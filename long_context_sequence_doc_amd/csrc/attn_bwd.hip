@@ -76,25 +76,28 @@ __device__ inline unsigned pack_bf16(float lo, float hi) {
 
 // ---------------------------------------------------------------------------
 // D_r = sum_d dO[r,h,d] * O[r,h,d] for the rows of the plan's Q tiles.
-// 32 threads per (row, head); D/32 elements each.
+// d / 8 threads per (row, head), each one 16-byte load of dO (8 bf16) and
+// two of O (8 fp32), then a butterfly over the group.
 __global__ __launch_bounds__(NT) void bwd_rowterm_kernel(const unsigned short *dout, int64_t q_row_stride,
                                                          const float *o, float *delta, const int32_t *tiles,
                                                          int32_t hq, int32_t d, int32_t tq) {
   const int r0 = tiles[2 * blockIdx.x], n = tiles[2 * blockIdx.x + 1];
-  const int pair = blockIdx.y * (NT / 32) + threadIdx.x / 32;   // (row, head) index inside the tile
-  const int lane = threadIdx.x & 31;
-  if (pair >= n * hq) return;
+  const int tpp = d / 8;                           // threads per (row, head): a power of two <= 64
+  const int pair = blockIdx.y * (NT / tpp) + threadIdx.x / tpp;   // (row, head) index inside the tile
+  const int sub = threadIdx.x % tpp;
+  if (pair >= n * hq) return;                      // whole groups leave together
   const int row = r0 + pair / hq, h = pair % hq;
-  const unsigned short *dp = dout + int64_t(row) * q_row_stride + int64_t(h) * d;
-  const float *op = o + (int64_t(row) * hq + h) * d;
+  const u32x4 dv = *reinterpret_cast<const u32x4 *>(dout + int64_t(row) * q_row_stride + int64_t(h) * d + 8 * sub);
+  const float *op = o + (int64_t(row) * hq + h) * d + 8 * sub;
+  const f32x4 o0 = *reinterpret_cast<const f32x4 *>(op), o1 = *reinterpret_cast<const f32x4 *>(op + 4);
   float acc = 0.f;
-  for (int e = lane; e < d; e += 32) {
-    const float dv = __builtin_bit_cast(float, unsigned(dp[e]) << 16);
-    acc += dv * op[e];
-  }
 #pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 32);
-  if (lane == 0) delta[int64_t(h) * tq + row] = acc;
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __builtin_bit_cast(float, dv[i] << 16), hi = __builtin_bit_cast(float, dv[i] & 0xffff0000u);
+    acc += lo * (i < 2 ? o0[2 * i] : o1[2 * i - 4]) + hi * (i < 2 ? o0[2 * i + 1] : o1[2 * i - 3]);
+  }
+  for (int m = tpp / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, tpp);
+  if (sub == 0) delta[int64_t(h) * tq + row] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -710,8 +713,9 @@ __global__ __launch_bounds__(128 * NH) void attn_bwd_dq_kernel(BwdParams p) {
 
 hipError_t launch_bwd_rowterm(const BwdLaunch &a, hipStream_t stream) {
   if (a.n_touched_q > 65535) return hipErrorInvalidValue;
-  const int pairs = a.max_q_rows * a.hq;
-  const dim3 grid{static_cast<unsigned>(a.n_touched_q), static_cast<unsigned>((pairs + NT / 32 - 1) / (NT / 32))};
+  if (a.d % 8 || a.d / 8 > 64) return hipErrorInvalidValue;
+  const int pairs = a.max_q_rows * a.hq, per_block = NT / (a.d / 8);
+  const dim3 grid{static_cast<unsigned>(a.n_touched_q), static_cast<unsigned>((pairs + per_block - 1) / per_block)};
   hipLaunchKernelGGL(bwd_rowterm_kernel, grid, dim3(NT), 0, stream,
                      static_cast<const unsigned short *>(a.dout), a.q_row_stride, a.o, a.delta, a.touched_rows,
                      a.hq, a.d, a.tq);
