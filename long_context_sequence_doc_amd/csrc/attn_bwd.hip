@@ -478,18 +478,22 @@ __global__ __launch_bounds__(NTK) void attn_bwd_kv_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dK += scale * sum of a split KV tile's partial dK^T slots, dV += sum of its
 // dV^T slots, the slots added in order (deterministic). One workgroup per
-// (split tile, KV head); each thread handles 4 consecutive d of one key.
+// (split tile, KV head, group of RK keys); each thread handles 4 consecutive
+// d of one key.
+constexpr int RK = 16;
 __global__ __launch_bounds__(NT) void bwd_kv_reduce_kernel(const ReduceItem *items, const float *partial,
                                                            int32_t n_slots, int32_t hkv, int32_t d, float scale,
                                                            float *dk, float *dv) {
   const ReduceItem it = items[blockIdx.x / hkv];
   const int g = blockIdx.x % hkv;
+  const int k0 = blockIdx.y * RK;
+  if (k0 >= it.n) return;
   const int64_t slot_stride = int64_t(hkv) * BNB * d;            // floats per slot
   const float *pk = partial + (int64_t(it.slot_begin) * hkv + g) * BNB * d;
   const float *pv = pk + int64_t(n_slots) * slot_stride;
-  const int quads = it.n * (d / 4);
+  const int quads = min(RK, it.n - k0) * (d / 4);
   for (int idx = threadIdx.x; idx < quads; idx += NT) {
-    const int key = idx / (d / 4), e4 = 4 * (idx % (d / 4));
+    const int key = k0 + idx / (d / 4), e4 = 4 * (idx % (d / 4));
     f32x4 sk = *reinterpret_cast<const f32x4 *>(pk + key * d + e4);
     f32x4 sv = *reinterpret_cast<const f32x4 *>(pv + key * d + e4);
     for (int c = 1; c < it.slot_count; ++c) {
@@ -761,7 +765,7 @@ hipError_t launch_attn_bwd(const BwdLaunch &a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     if (a.n_reduce > 0) {
       if (int64_t(a.n_reduce) * a.hkv > INT32_MAX) return hipErrorInvalidValue;
-      hipLaunchKernelGGL(bwd_kv_reduce_kernel, dim3(static_cast<unsigned>(a.n_reduce * a.hkv)), dim3(NT), 0, stream,
+      hipLaunchKernelGGL(bwd_kv_reduce_kernel, dim3(static_cast<unsigned>(a.n_reduce * a.hkv), BNB / RK), dim3(NT), 0, stream,
                          a.kv_reduce, a.partial, a.n_slots, a.hkv, a.d, a.scale, a.dk, a.dv);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
