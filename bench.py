@@ -47,6 +47,8 @@ def _args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="zigzag", choices=["zigzag", "ring", "ulysses", "train", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ranks", action="store_true",
+                    help="skip the per-rank sweep of the sharded workloads (zigzag / ring vs balanced layout)")
     ap.add_argument("--forward-only", action="store_true",
                     help="skip the training-step (forward + backward) measurement of forward workloads")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -142,6 +144,96 @@ class _Timer:
 
     def count(self, name):
         return len(self.ev.get(name, []))
+
+
+BALANCE_CHUNK = 1024   # rows per chunk of the document-aware balanced layout
+
+
+def rank_sweep(w, t, a, stream):
+    """Every rank of the sequence-parallel layout ``w`` comes from (its own
+    zigzag or contiguous-ring layout) and of the document-aware balanced
+    layout from sap_balance, timed one after another on this GPU: per rank and
+    ring step, the fused forward (merges in the epilogue). Job time is the
+    slowest rank when each rank fetches the KV it needs without lock-step
+    (sum over steps, max over ranks), or the sum over ring steps of the
+    slowest rank's step when the ring moves in lock-step. Each rank is also
+    timed as one call over all the KV it needs."""
+    import torch
+    import workloads as W
+    import long_context_sequence_doc_amd as sap
+    from long_context_sequence_doc_amd.rank import RankForward
+    p, chunk = w.extra["p"], w.extra["chunk"]
+    if w.name.startswith("zigzag"):
+        base = ("zigzag", W.zigzag_owner(p), chunk)
+    else:
+        base = ("ring", list(range(p)), chunk)
+    owner, _ = sap.sap_balance(w.cu, p, BALANCE_CHUNK)
+    dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    k, v = dev(t.k), dev(t.v)
+    out = {}
+    for tag, own, ch in (base, ("balanced", owner.tolist(), BALANCE_CHUNK)):
+        flop, rank_ms, step_ms, fetched, one_ms = [], [], [], [], []
+        for r in range(p):
+            wr = W.owner_rank(w, own, r, ch, tag)
+            rf = RankForward(wr.cu, wr.q_segs, [s.kv_segs for s in wr.steps], wr.hq, wr.hkv, wr.d, wr.scale)
+            q = dev(W.local_rows(t.q, wr.q_segs))
+            qs, ks = q.stride(0), k.stride(0)
+
+            def fwd(tm):
+                for n, i in enumerate(rf.active):
+                    f = sap.sap_attn_fwd if n == 0 else sap.sap_attn_fwd_merge
+                    tm.run(i, lambda: f(rf.plans[i], q, k, v, qs, ks, wr.hq, wr.hkv, wr.d, wr.scale, rf.o, rf.lse))
+            warm = _Timer(stream)
+            for _ in range(a.warmup):
+                fwd(warm)
+            torch.cuda.synchronize()
+            tm = _Timer(stream)
+            for _ in range(a.steps):
+                fwd(tm)
+            torch.cuda.synchronize()
+            per_step = [tm.ms(i) / a.steps if i in rf.active else 0.0 for i in range(p)]
+            flop.append(rf.useful_flop)
+            step_ms.append(per_step)
+            rank_ms.append(sum(per_step))
+            fetched.append(sum(e - b for i in rf.active if i > 0 for b, e, _ in wr.steps[i].kv_segs))
+            rf.close()
+            # the same rank as one call over all the KV it needs (no ring steps, no merge)
+            rc = RankForward.concatenated(wr.cu, wr.q_segs, [s.kv_segs for s in wr.steps], wr.hq, wr.hkv, wr.d,
+                                          wr.scale)
+
+            def one(tm):
+                tm.run(0, lambda: sap.sap_attn_fwd(rc.plans[0], q, k, v, qs, ks, wr.hq, wr.hkv, wr.d, wr.scale,
+                                                   rc.o, rc.lse))
+            for _ in range(a.warmup):
+                one(warm)
+            torch.cuda.synchronize()
+            tm = _Timer(stream)
+            for _ in range(a.steps):
+                one(tm)
+            torch.cuda.synchronize()
+            one_ms.append(tm.ms(0) / a.steps)
+            rc.close()
+            del q
+        job = max(rank_ms)
+        lockstep = sum(max(step_ms[r][s] for r in range(p)) for s in range(p))
+        out[tag] = {
+            "chunk_rows": ch,
+            "useful_flop": flop,
+            "ms": [round(x, 4) for x in rank_ms],
+            "tflops": [round(f / (m * 1e-3) / 1e12, 1) for f, m in zip(flop, rank_ms)],
+            "work_max_over_mean": round(max(flop) / (sum(flop) / p), 4),
+            "job_ms": round(job, 4),
+            "job_tflops_per_gpu": round(sum(flop) / (job * 1e-3) / 1e12 / p, 1),
+            "lockstep_ring_ms": round(lockstep, 4),
+            "lockstep_ring_tflops_per_gpu": round(sum(flop) / (lockstep * 1e-3) / 1e12 / p, 1),
+            "remote_kv_rows_fetched": fetched,
+            "single_call_ms": [round(x, 4) for x in one_ms],
+            "single_call_job_tflops_per_gpu": round(sum(flop) / (max(one_ms) * 1e-3) / 1e12 / p, 1),
+        }
+    out["note"] = ("each rank's forward (ring steps, fused merges) timed alone on this one GPU; job_ms = slowest "
+                   "rank (KV fetched as needed), lockstep_ring_ms = sum over ring steps of the slowest rank's step, "
+                   "single_call_ms = the rank as one call over all the KV it needs; communication not included")
+    return out
 
 
 def main():
@@ -374,6 +466,8 @@ def main():
                                  "pct_of_peak": round(100.0 * tvalue / PEAK_BF16_TFLOPS, 2),
                                  "ms_per_step": round(ms_t, 4), "useful_flop_per_step": tflop,
                                  "flop_per_pair_per_head": 14 * w.d, "kernels": tkernels}
+    if not a.no_ranks and not a.forward_only and "p" in w.extra and "chunk" in w.extra:
+        line["ranks"] = rank_sweep(w, t, a, stream)
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, t, not headline_bwd)
     rf.close()

@@ -137,6 +137,30 @@ sap_status sap_plan_q_tiles(sap_plan_t plan, int32_t *touched, int32_t cap_touch
 void sap_plan_free(sap_plan_t plan);
 
 /*
+ * sap_balance -- document-aware assignment of query chunks to ranks (host
+ * only). Uneven document lengths leave some GPUs idle (SP blog page,
+ * bmjup.com/post/14448.html, future trends and challenges); the HSAP summary
+ * page (gptget.net/papers/2606.30460, technical contributions) balances the
+ * devices by scheduling. The sequence is cut into chunks of chunk_rows
+ * consecutive positions; chunk c's work is its allowed (query, key) pairs
+ * per head, the sum over its positions i of i - ds(i) + 1. Every rank gets
+ * n_chunks / n_ranks chunks (equal token counts); chunks are taken heaviest
+ * first (ties: lower chunk index) and each goes to the rank with the least
+ * work so far among those with room (ties: lower rank). A rank then holds
+ * its chunks in ascending position order: its Q segment table, and the KV
+ * rows it contributes to the other ranks.
+ * cu_seqlens: as for sap_plan. The total length must be a positive multiple
+ *   of chunk_rows * n_ranks.
+ * owner: host int32 [n_chunks] (n_chunks = total / chunk_rows), receives the
+ *   rank of every chunk; cap_owner = its capacity.
+ * rank_work: host int64 [n_ranks] or NULL, receives each rank's work.
+ * O(n_chunks log n_chunks + n_docs). Errors: SAP_ERR_INVALID_ARG,
+ *   SAP_ERR_NO_MEMORY (nothing written on error).
+ */
+sap_status sap_balance(const int32_t *cu_seqlens, int32_t n_docs, int32_t n_ranks, int32_t chunk_rows,
+                       int32_t *owner, int64_t cap_owner, int64_t *rank_work);
+
+/*
  * sap_attn_fwd -- partial attention of the plan's Q rows against this call's
  * KV rows (one ring step, or the whole sequence for a head-sharded rank).
  * For every listed tile pair it takes S = q k^T on bf16 matrix cores (fp32

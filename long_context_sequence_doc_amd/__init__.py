@@ -19,7 +19,7 @@ import numpy as np
 __all__ = [
     "SapError", "Segment", "PlanStats", "Plan",
     "sap_plan", "sap_plan_upload", "sap_plan_info", "sap_plan_tiles", "sap_plan_q_tiles",
-    "sap_plan_free", "sap_attn_fwd", "sap_attn_fwd_merge", "sap_lse_merge", "sap_attn_bwd_workspace", "sap_attn_bwd",
+    "sap_plan_free", "sap_balance", "sap_attn_fwd", "sap_attn_fwd_merge", "sap_lse_merge", "sap_attn_bwd_workspace", "sap_attn_bwd",
     "sap_attn_bwd_rowterm", "sap_attn_bwd_accumulate",
     "sap_last_error", "sap_version", "lib_path", "SAP_TILE_FULL", "SAP_TILE_DIAGONAL",
     "SAP_TILE_PARTIAL",
@@ -74,6 +74,7 @@ _sigs = {
     "sap_plan_tiles": ([_P, _P, _P, _P, _i64], _i32),
     "sap_plan_q_tiles": ([_P, _P, _i32, _P, _i32], _i32),
     "sap_plan_free": ([_P], None),
+    "sap_balance": ([ctypes.POINTER(_i32), _i32, _i32, _i32, _P, _i64, _P], _i32),
     "sap_attn_fwd": ([_P, _P, _P, _P, _i64, _i64, _i32, _i32, _i32, _f32, _P, _P, _P], _i32),
     "sap_attn_fwd_merge": ([_P, _P, _P, _P, _i64, _i64, _i32, _i32, _i32, _f32, _P, _P, _P], _i32),
     "sap_lse_merge": ([_P, _P, _P, _P, _P, _i32, _i32, _i32, _P], _i32),
@@ -194,6 +195,18 @@ def sap_plan_q_tiles(plan: Plan):
 
 def sap_plan_free(plan: Plan):
     plan.free()
+
+
+def sap_balance(cu_seqlens, n_ranks: int, chunk_rows: int):
+    """Owner rank of every ``chunk_rows`` chunk (int32 array) and each rank's work (int64 array)."""
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    total = int(cu[-1])
+    n_chunks = total // chunk_rows if chunk_rows > 0 else 0
+    owner = np.zeros(max(n_chunks, 1), dtype=np.int32)
+    work = np.zeros(max(n_ranks, 1), dtype=np.int64)
+    _check(_lib.sap_balance(cu.ctypes.data_as(ctypes.POINTER(_i32)), len(cu) - 1, n_ranks, chunk_rows,
+                            owner.ctypes.data, len(owner), work.ctypes.data))
+    return owner[:n_chunks], work[:n_ranks]
 
 
 def sap_attn_fwd(plan: Plan, q, k, v, q_row_stride: int, kv_row_stride: int, hq: int, hkv: int, d: int,

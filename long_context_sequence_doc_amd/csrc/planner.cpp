@@ -21,8 +21,11 @@
 //   PARTIAL  otherwise                     a document start cuts the tile
 #include <algorithm>
 #include <cstring>
-#include <numeric>
+#include <functional>
 #include <new>
+#include <numeric>
+#include <queue>
+#include <utility>
 
 #include "sap_internal.h"
 
@@ -279,6 +282,64 @@ sap_status build_plan(const int32_t *cu_in, int32_t n_docs, const sap_segment *q
     P.kv_work.push_back(cw[size_t(i)]);
     P.kv_range.push_back(cr[size_t(i)]);
     P.kv_slot.push_back(cs[size_t(i)]);
+  }
+  return SAP_OK;
+}
+
+// Document-aware assignment of query chunks to ranks.
+//
+// The SP blog page (bmjup.com/post/14448.html, future trends and challenges)
+// notes that uneven sequence lengths leave GPUs idle; the HSAP summary page
+// (gptget.net/papers/2606.30460, technical contributions) balances devices by
+// scheduling. Every rank keeps the same number of chunks (the same token
+// count); chunks go heaviest first (ties: lower index) to the least-loaded
+// rank that still has room (ties: lower rank). A chunk's work is its allowed
+// pairs, summed per document run in closed form: the rows [x, y) of a
+// document starting at d see x-d+1 .. y-d keys, T(y-d) - T(x-d) in total with
+// T(n) = n (n + 1) / 2.
+sap_status balance_chunks(const int32_t *cu, int32_t n_docs, int32_t n_ranks, int32_t chunk,
+                          std::vector<int32_t> *owner, std::vector<int64_t> *load, std::string *err) {
+  if (!cu || n_docs < 1) { *err = "cu_seqlens: need at least one document"; return SAP_ERR_INVALID_ARG; }
+  if (cu[0] != 0) { *err = "cu_seqlens[0] must be 0"; return SAP_ERR_INVALID_ARG; }
+  for (int32_t i = 0; i < n_docs; ++i)
+    if (cu[i + 1] < cu[i]) { *err = "cu_seqlens must be non-decreasing"; return SAP_ERR_INVALID_ARG; }
+  if (n_ranks < 1 || chunk < 1) { *err = "need n_ranks >= 1 and chunk_rows >= 1"; return SAP_ERR_INVALID_ARG; }
+  const int64_t total = cu[n_docs];
+  if (total == 0 || total % (int64_t(chunk) * n_ranks) != 0) {
+    *err = "total length must be a positive multiple of chunk_rows * n_ranks";
+    return SAP_ERR_INVALID_ARG;
+  }
+  const int64_t n_chunks = total / chunk;
+  const int64_t cap = n_chunks / n_ranks;
+  auto tri = [](int64_t n) { return n * (n + 1) / 2; };
+  std::vector<int64_t> work(size_t(n_chunks), 0);
+  int32_t di = 0;
+  for (int64_t c = 0; c < n_chunks; ++c) {
+    const int64_t x0 = c * chunk, y0 = x0 + chunk;
+    while (cu[di + 1] <= x0) ++di;  // document holding x0 (empty ones skipped)
+    for (int32_t dj = di; dj < n_docs && cu[dj] < y0; ++dj) {
+      const int64_t x = std::max<int64_t>(x0, cu[dj]), y = std::min<int64_t>(y0, cu[dj + 1]);
+      if (y > x) work[size_t(c)] += tri(y - cu[dj]) - tri(x - cu[dj]);
+    }
+  }
+  std::vector<int32_t> order(static_cast<size_t>(n_chunks));
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t a, int32_t b) { return work[size_t(a)] > work[size_t(b)]; });
+  // ranks with room, least loaded first (ties: lower rank)
+  typedef std::pair<int64_t, int32_t> Entry;
+  std::priority_queue<Entry, std::vector<Entry>, std::greater<Entry>> open;
+  for (int32_t r = 0; r < n_ranks; ++r) open.push(Entry(0, r));
+  std::vector<int64_t> count(size_t(n_ranks), 0);
+  owner->assign(size_t(n_chunks), -1);
+  load->assign(size_t(n_ranks), 0);
+  for (int32_t c : order) {
+    const Entry e = open.top();
+    open.pop();
+    const int32_t r = e.second;
+    (*owner)[size_t(c)] = r;
+    (*load)[size_t(r)] = e.first + work[size_t(c)];
+    if (++count[size_t(r)] < cap) open.push(Entry((*load)[size_t(r)], r));
   }
   return SAP_OK;
 }

@@ -89,6 +89,26 @@ sap_status sap_plan(const int32_t *cu_seqlens, int32_t n_docs, const sap_segment
   return ok();
 }
 
+sap_status sap_balance(const int32_t *cu_seqlens, int32_t n_docs, int32_t n_ranks, int32_t chunk_rows,
+                       int32_t *owner, int64_t cap_owner, int64_t *rank_work) {
+  if (!owner) return fail(SAP_ERR_INVALID_ARG, "owner is NULL");
+  std::vector<int32_t> own;
+  std::vector<int64_t> load;
+  std::string err;
+  sap_status s;
+  try {
+    s = sap::balance_chunks(cu_seqlens, n_docs, n_ranks, chunk_rows, &own, &load, &err);
+  } catch (const std::bad_alloc &) {
+    s = SAP_ERR_NO_MEMORY;
+    err = "host memory exhausted while balancing";
+  }
+  if (s != SAP_OK) return fail(s, err);
+  if (cap_owner < int64_t(own.size())) return fail(SAP_ERR_INVALID_ARG, "owner capacity smaller than the chunk count");
+  std::copy(own.begin(), own.end(), owner);
+  if (rank_work) std::copy(load.begin(), load.end(), rank_work);
+  return ok();
+}
+
 sap_status sap_plan_upload(sap_plan_t plan, void *hip_stream) {
   if (!plan) return fail(SAP_ERR_INVALID_ARG, "plan is NULL");
   sap::Plan &P = plan->p;

@@ -101,4 +101,9 @@ sap_status build_plan(const int32_t *cu, int32_t n_docs, const sap_segment *q_se
                       int32_t n_q, const sap_segment *kv_segs, int32_t n_kv, int32_t bm,
                       int32_t bn, Plan *out, std::string *err);
 
+// Owner rank of every chunk_rows-position chunk and the work per rank
+// (sap_balance); returns SAP_OK or an error with *err filled.
+sap_status balance_chunks(const int32_t *cu, int32_t n_docs, int32_t n_ranks, int32_t chunk,
+                          std::vector<int32_t> *owner, std::vector<int64_t> *load, std::string *err);
+
 }  // namespace sap

@@ -60,3 +60,51 @@ def test_random_layouts_exact(seed):
             kv_segs.append((a, b, loc_k))
             loc_k += b - a + int(rng.integers(0, 40))
     _compare(cu, q_segs, kv_segs, bm, bn)
+
+
+# --- document-aware chunk-to-rank assignment (sap_balance) ------------------
+
+from oracle import balance as B  # noqa: E402
+
+
+def _balance_exact(cu, p, chunk):
+    owner, work = sap.sap_balance(cu, p, chunk)
+    ref_owner, ref_work = B.balance(cu, p, chunk)
+    assert owner.tolist() == ref_owner
+    assert work.tolist() == ref_work
+    return owner
+
+
+@pytest.mark.parametrize("name,p,chunk", [("ring", 8, 512), ("zigzag", 8, 1024), ("zigzag", 8, 256),
+                                          ("train", 8, 1024), ("train", 4, 128), ("ulysses", 8, 4096)])
+def test_balance_workloads_exact(name, p, chunk):
+    w = W.by_name(name)
+    _balance_exact(w.cu, p, chunk)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_balance_random_exact(seed):
+    rng = np.random.default_rng(300 + seed)
+    p = int(rng.choice([1, 2, 3, 4, 7, 8, 16]))
+    chunk = int(rng.choice([1, 8, 64, 128]))
+    total = p * chunk * int(rng.integers(1, 12))
+    cu = W.cu_seqlens(W.random_docs(rng, total, max_len=max(1, total // int(rng.integers(1, 6)))))
+    _balance_exact(cu, p, chunk)
+
+
+def test_balanced_rank_plans_exact():
+    """Every ring step of a balanced 128K rank plans exactly like the oracle."""
+    w = W.zigzag_rank(3)
+    owner = _balance_exact(w.cu, 8, 1024)
+    b = W.owner_rank(w, owner.tolist(), 3, 1024, "balanced")
+    assert len(b.q_segs) > 1
+    for st in b.steps:
+        _compare(b.cu, b.q_segs, st.kv_segs, 128, 64)
+    _compare(b.cu, b.q_segs, b.steps[2].kv_segs, 64, 128)
+
+
+@pytest.mark.parametrize("cu,p,chunk", [([0, 10], 2, 4), ([0, 8], 0, 4), ([0, 8], 2, 0), ([1, 8], 2, 4),
+                                        ([0, 8, 4], 2, 2)])
+def test_balance_rejects_bad_arguments(cu, p, chunk):
+    with pytest.raises(sap.SapError):
+        sap.sap_balance(cu, p, chunk)

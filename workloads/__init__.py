@@ -162,6 +162,47 @@ def _zigzag_steps(p: int, rank: int, chunk: int) -> List[Step]:
     return steps
 
 
+def _runs(chunks: List[int], chunk: int, local: bool) -> List[Segment]:
+    """Segments of ascending chunk indices, consecutive chunks merged.
+
+    local=True packs them into consecutive local rows from 0 (a rank's own
+    buffer); local=False keeps local row = global position (a whole-sequence
+    buffer viewed in place)."""
+    segs: List[Segment] = []
+    ls = 0
+    for c in sorted(chunks):
+        gs, ge = c * chunk, (c + 1) * chunk
+        if segs and segs[-1][1] == gs:
+            segs[-1] = (segs[-1][0], ge, segs[-1][2])
+        else:
+            segs.append((gs, ge, ls if local else gs))
+        ls += chunk
+    return segs
+
+
+def zigzag_owner(p: int) -> List[int]:
+    """Owner rank of each of the 2P chunks of the zigzag layout (r owns r and 2P-1-r)."""
+    return [j if j < p else 2 * p - 1 - j for j in range(2 * p)]
+
+
+def owner_rank(base: "Workload", owner: List[int], rank: int, chunk: int, tag: str) -> "Workload":
+    """The workload of one rank of a chunk-to-rank layout given as ``owner[c]``.
+
+    The rank holds its chunks' Q rows in ascending order; at ring step s it
+    holds the KV chunks of rank (rank - s) mod P, viewed in place in the
+    whole-sequence K/V (the same ring direction as the other layouts)."""
+    p = max(owner) + 1
+    mine = [c for c, r in enumerate(owner) if r == rank]
+    steps = []
+    for s in range(p):
+        src = (rank - s) % p
+        theirs = [c for c, r in enumerate(owner) if r == src]
+        steps.append(Step(s, theirs, _runs(theirs, chunk, local=False)))
+    return Workload(f"{tag}_rank{rank}", f"{base.description}, {tag} layout",
+                    base.lengths, base.hq, base.hkv, base.d, _runs(mine, chunk, local=True), steps,
+                    extra={"p": p, "rank": rank, "chunk": chunk, "layout": tag})
+
+
 def tiny() -> Workload:
     lengths = [64, 192, 32, 224]
     return Workload("tiny_packed_512", "512 tokens, 4 documents, 2 heads, head_dim 64, P=1",
