@@ -45,7 +45,7 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="zigzag", choices=["zigzag", "ring", "ulysses", "train", "tiny"])
+    ap.add_argument("--workload", default="zigzag", choices=["zigzag", "ring", "ulysses", "ulysses_gqa", "train", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ranks", action="store_true",
                     help="skip the per-rank sweep of the sharded workloads (zigzag / ring vs balanced layout)")

@@ -298,11 +298,13 @@ def test_training_forward_sampled():
     rf.close()
 
 
-def test_ulysses_sampled():
-    """512K Ulysses head shard: rows sampled from every document, the end of each long one."""
+@pytest.mark.parametrize("name", ["ulysses", "ulysses_gqa"])
+def test_ulysses_sampled(name):
+    """512K Ulysses head shard (4 heads, or 4 query heads sharing one KV head):
+    rows sampled from every document, the end of each long one."""
     _sap()
-    say("case ulysses_512k_4heads forward, sampled rows")
-    w, t, rf, q, k, v = _rank_run("ulysses")
+    say(f"case {W.by_name(name).name} forward, sampled rows")
+    w, t, rf, q, k, v = _rank_run(name)
     g = np.arange(w.total)
     cu = w.cu
     rng = np.random.default_rng(5)
@@ -313,7 +315,7 @@ def test_ulysses_sampled():
         rows.update(rng.integers(s, e, size=64).tolist())
     rows = np.array(sorted(rows))
     ro, rl = A.forward(f64(t.q), f64(t.k), f64(t.v), g, g, cu, w.scale, rows=rows)
-    compare(rf.o.cpu().numpy(), rf.lse.cpu().numpy(), ro, rl, rows=rows, label="ulysses")
+    compare(rf.o.cpu().numpy(), rf.lse.cpu().numpy(), ro, rl, rows=rows, label=w.name)
     rf.close()
 
 

@@ -15,6 +15,8 @@ def test_lengths_fill_sequence_and_respect_bounds():
     u = W.ulysses()
     assert u.lengths[:2] == [262144, 131072] and sum(u.lengths) == 524288
     assert all(64 <= L <= 2048 for L in u.lengths[2:-1])
+    g = W.by_name("ulysses_gqa")
+    assert (g.hq, g.hkv) == (4, 1) and g.lengths == u.lengths and g.name != u.name
 
 
 def test_bf16_rounding_matches_torch():

@@ -233,10 +233,17 @@ def zigzag_rank(rank: int = 3) -> Workload:
 
 
 def ulysses(hkv: int = 4) -> Workload:
+    """One Ulysses rank: the whole 512K sequence for its 4 query heads.
+
+    hkv=4 is the plain head split; hkv=1 is a GQA-aware split of a 32-query /
+    8-KV-head model over 8 ranks, where each rank keeps one KV group (4 query
+    heads sharing one KV head) and so needs one KV head only."""
     lengths = ulysses_lengths()
     total = sum(lengths)
-    return Workload("ulysses_512k_4heads", "524288 tokens, hybrid context, 4 heads, head_dim 128",
-                    lengths, 4, hkv, 128, [(0, total, 0)], [Step(0, [0], [(0, total, 0)])])
+    name = "ulysses_512k_4heads" if hkv == 4 else f"ulysses_512k_4q{hkv}kv"
+    desc = "524288 tokens, hybrid context, 4 heads, head_dim 128" if hkv == 4 else \
+        f"524288 tokens, hybrid context, 4 query heads / {hkv} KV head(s), head_dim 128"
+    return Workload(name, desc, lengths, 4, hkv, 128, [(0, total, 0)], [Step(0, [0], [(0, total, 0)])])
 
 
 def training() -> Workload:
@@ -247,7 +254,7 @@ def training() -> Workload:
 
 
 ALL = {"tiny": tiny, "ring": ring_rank, "zigzag": zigzag_rank, "ulysses": ulysses,
-       "train": training}
+       "ulysses_gqa": lambda: ulysses(hkv=1), "train": training}
 
 
 def by_name(name: str, **kw) -> Workload:
