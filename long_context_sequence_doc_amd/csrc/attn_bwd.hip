@@ -42,6 +42,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <cstdint>
 #include <cmath>
 #include <type_traits>
 
@@ -238,9 +239,18 @@ __global__ __launch_bounds__(NTK) void attn_bwd_kv_kernel(BwdParams p) {
   };
 
   // The (Q tile, query head) iterations run in order it * group + hi.
+  // Partner entries come through the scalar cache (the index is uniform), so
+  // no vector load has to wait behind the in-flight row copies.
   const int n_iter = rg.count * p.group;
+  typedef __attribute__((address_space(4))) const PartnerEntry const_entry;
+  const const_entry *cpart = (const const_entry *)p.partners;
+  const int pbase = __builtin_amdgcn_readfirstlane(rg.begin);
+  auto entry = [&](int itr) {
+    const const_entry &e = cpart[__builtin_amdgcn_readfirstlane(pbase + itr / p.group)];
+    return PartnerEntry{e.local_start, e.global_start, e.n, e.cls};
+  };
   auto issue_rows = [&](int itr, unsigned char *stage) {
-    const PartnerEntry t = p.partners[rg.begin + itr / p.group];
+    const PartnerEntry t = entry(itr);
     const int hh = g * p.group + itr % p.group;
     const int64_t base = int64_t(t.local_start) * p.q_row_stride + int64_t(hh) * D;
 #pragma unroll
@@ -252,23 +262,26 @@ __global__ __launch_bounds__(NTK) void attn_bwd_kv_kernel(BwdParams p) {
       __builtin_amdgcn_global_load_lds((global_void *)(p.dout + off), dd, 16, 0, 0);
     }
   };
-  // per-row terms of one iteration (threads 0..BMB-1, one row each)
+  // per-row terms of one iteration (threads 0..BMB-1, one row each): loaded
+  // raw at the start of the previous iteration and turned into the stage's
+  // form only when stored at its end, so nothing waits for them (or for the
+  // row copies issued before them) in between
   float rt_l = 0.f, rt_d = 0.f;
   int rt_s = 0;
+  PartnerEntry rt_t{};
   auto load_terms = [&](int itr) {
-    const PartnerEntry t = p.partners[rg.begin + itr / p.group];
+    rt_t = entry(itr);
     const int hh = g * p.group + itr % p.group;
-    const int row = min(tid, t.n - 1);
-    const int64_t li = int64_t(hh) * p.tq + t.local_start + row;
-    const float l = p.lse[li];
-    // rows past the tile end or with no key at all get P = 0
-    rt_l = (tid < t.n && l != -INFINITY) ? l * LOG2E : INFINITY;
+    const int row = min(tid, rt_t.n - 1);
+    const int64_t li = int64_t(hh) * p.tq + rt_t.local_start + row;
+    rt_l = p.lse[li];
     rt_d = p.delta[li];
     // document start bounds keys only in PARTIAL tiles
-    rt_s = t.cls == SAP_TILE_PARTIAL ? p.ds_q[t.local_start + row] : INT_MIN;
+    rt_s = rt_t.cls == SAP_TILE_PARTIAL ? p.ds_q[rt_t.local_start + row] : INT_MIN;
   };
   auto store_terms = [&](unsigned char *stage) {
-    reinterpret_cast<float *>(stage + KS::LSE2)[tid] = rt_l;
+    // rows past the tile end or with no key at all get P = 0
+    reinterpret_cast<float *>(stage + KS::LSE2)[tid] = (tid < rt_t.n && rt_l != -INFINITY) ? rt_l * LOG2E : INFINITY;
     reinterpret_cast<float *>(stage + KS::DELTA)[tid] = rt_d;
     reinterpret_cast<int *>(stage + KS::DS)[tid] = rt_s;
   };
@@ -281,7 +294,7 @@ __global__ __launch_bounds__(NTK) void attn_bwd_kv_kernel(BwdParams p) {
   __syncthreads();
 
   for (int itr = 0; itr < n_iter; ++itr) {
-    const PartnerEntry qt = p.partners[rg.begin + itr / p.group];
+    const PartnerEntry qt = entry(itr);
     unsigned char *cur = lds + ST0 + (itr & 1) * STAGE;
     unsigned char *nxt = lds + ST0 + ((itr + 1) & 1) * STAGE;
     const bool more = itr + 1 < n_iter;
@@ -372,21 +385,37 @@ __global__ __launch_bounds__(NTK) void attn_bwd_kv_kernel(BwdParams p) {
 
     // ---- dV^T += dO^T P, dK^T += Q^T dS (k = 16 query rows per step; the
     //      rows of step u are qb*32 + 16u + 4hf + (0..3 | 8..11))
+    //      The transposing reads go through inline asm with explicit waits:
+    //      the compiler cannot tell them apart from the in-flight copies into
+    //      the other stage and would wait for those first.
     {
-      bf16x8 ado = tr_pair(cur + KS::DO, qb * 32, 0), aqt = tr_pair(cur + KS::Q, qb * 32, 0);
+      const unsigned cbase = static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_void *)cur));
+      auto tr_issue = [&](unsigned tile, int base_row, int db, u32x2 &lo, u32x2 &hi) {
+        const unsigned a = tile + t_off[db] + base_row * RT::ROW;
+        const unsigned b2 = RT::CPR >= 16 ? tile + (t_off[db] ^ 128) + (base_row + 8) * RT::ROW : a + 8 * RT::ROW;
+        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a));
+        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hi) : "v"(b2));
+      };
+      auto issue = [&](int k, u32x2 (&r)[4]) {
+        const int u = k / (D / 32), db = k % (D / 32);
+        tr_issue(cbase + KS::DO, qb * 32 + 16 * u, db, r[0], r[1]);
+        tr_issue(cbase + KS::Q, qb * 32 + 16 * u, db, r[2], r[3]);
+      };
+      auto join = [](const u32x2 &lo, const u32x2 &hi) { return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y}); };
+      u32x2 rr[2][4];
+      issue(0, rr[0]);
 #pragma unroll
       for (int k = 0; k < 2 * (D / 32); ++k) {
         const int u = k / (D / 32), db = k % (D / 32);
-        bf16x8 n_do = ado, n_qt = aqt;
+        u32x2 (&r)[4] = rr[k & 1];
         if (k + 1 < 2 * (D / 32)) {
-          const int u1 = (k + 1) / (D / 32), db1 = (k + 1) % (D / 32);
-          n_do = tr_pair(cur + KS::DO, qb * 32 + 16 * u1, db1);
-          n_qt = tr_pair(cur + KS::Q, qb * 32 + 16 * u1, db1);
+          issue(k + 1, rr[(k + 1) & 1]);
+          asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
+        } else {
+          asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
         }
-        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, pb[u], dva[db], 0, 0, 0);
-        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, sb[u], dka[db], 0, 0, 0);
-        ado = n_do;
-        aqt = n_qt;
+        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(r[0], r[1]), pb[u], dva[db], 0, 0, 0);
+        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(r[2], r[3]), sb[u], dka[db], 0, 0, 0);
       }
     }
 
@@ -609,12 +638,22 @@ __global__ __launch_bounds__(128 * NH) void attn_bwd_dq_kernel(BwdParams p) {
     }
   };
 
+  // partner entries through the scalar cache (uniform index): no vector
+  // load waits behind the in-flight copies
+  typedef __attribute__((address_space(4))) const PartnerEntry const_entry;
+  const const_entry *cpart = (const const_entry *)p.partners;
+  const int pbase = __builtin_amdgcn_readfirstlane(rg.begin);
+  auto entry = [&](int i) {
+    const const_entry &e = cpart[__builtin_amdgcn_readfirstlane(pbase + i)];
+    return PartnerEntry{e.local_start, e.global_start, e.n, e.cls};
+  };
+
   // iterations: the 64-key halves of the partner tiles, in order
   int it = 0, half = 0, stage_i = 0;
-  if (rg.count > 0) issue_half(p.partners[rg.begin], 0, lds);
+  if (rg.count > 0) issue_half(entry(0), 0, lds);
   __syncthreads();
   while (it < rg.count) {
-    const PartnerEntry kt = p.partners[rg.begin + it];
+    const PartnerEntry kt = entry(it);
     unsigned char *cur = lds + stage_i * STAGE;
     // the next half: this tile's second one, or the next tile's first
     int nit = it, nhalf = half + 1;
@@ -622,7 +661,7 @@ __global__ __launch_bounds__(128 * NH) void attn_bwd_dq_kernel(BwdParams p) {
       nit = it + 1;
       nhalf = 0;
     }
-    if (nit < rg.count) issue_half(p.partners[rg.begin + nit], nhalf, lds + (stage_i ^ 1) * STAGE);
+    if (nit < rg.count) issue_half(entry(nit), nhalf, lds + (stage_i ^ 1) * STAGE);
 
     const int k0 = half * HKQ;                    // first key of this part within the tile
     const int kn = min(HKQ, kt.n - k0);           // keys in this part
@@ -674,22 +713,50 @@ __global__ __launch_bounds__(128 * NH) void attn_bwd_dq_kernel(BwdParams p) {
         sb[kb][u] = as_bf16x8(sk);
       }
 
-    // ---- dQ^T += K^T dS^T (k = 16 keys per step: kb*32 + 16u + 4hf + (0..3 | 8..11))
-#pragma unroll
-    for (int kb = 0; kb < KBQ; ++kb)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
+    // ---- dQ^T += K^T dS^T (k = 16 keys per step: kb*32 + 16u + 4hf + (0..3 | 8..11)).
+    //      The transposing reads go through inline asm with explicit waits:
+    //      the compiler cannot tell them apart from the in-flight copies into
+    //      the other stage and would wait for those first.
+    {
+      constexpr int NSTEP = 2 * KBQ, NR = 2 * (D / 32);
+      const unsigned kbase = static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_void *)(cur + KOFF)));
+      auto issue = [&](int st, u32x2 (&r)[NR]) {
+        const int row0 = 16 * st;                 // kb * 32 + 16 u
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const unsigned char *a = cur + KOFF + t_off[db] + (kb * 32 + 16 * u) * RT::ROW;
-          const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a));
-          const unsigned char *a8 = RT::CPR >= 16
-              ? cur + KOFF + ((t_off[db] ^ 128) + (kb * 32 + 16 * u + 8) * RT::ROW)
-              : a + 8 * RT::ROW;
-          const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a8));
-          const bf16x8 ak = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+          const unsigned a = kbase + t_off[db] + row0 * RT::ROW;
+          const unsigned a8 = RT::CPR >= 16 ? kbase + (t_off[db] ^ 128) + (row0 + 8) * RT::ROW : a + 8 * RT::ROW;
+          asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r[2 * db]) : "v"(a));
+          asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r[2 * db + 1]) : "v"(a8));
+        }
+      };
+      u32x2 rr[2][NR];
+      issue(0, rr[0]);
+#pragma unroll
+      for (int st = 0; st < NSTEP; ++st) {
+        u32x2 (&r)[NR] = rr[st & 1];
+        if (st + 1 < NSTEP) {
+          issue(st + 1, rr[(st + 1) & 1]);
+          if constexpr (NR == 8)
+            asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]),
+                         "+v"(r[5]), "+v"(r[6]), "+v"(r[7]));
+          else
+            asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
+        } else {
+          if constexpr (NR == 8)
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]),
+                         "+v"(r[5]), "+v"(r[6]), "+v"(r[7]));
+          else
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
+        }
+        const int kb = st >> 1, u = st & 1;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const bf16x8 ak = as_bf16x8(u32x4{r[2 * db].x, r[2 * db].y, r[2 * db + 1].x, r[2 * db + 1].y});
           qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, sb[kb][u], qacc[db], 0, 0, 0);
         }
+      }
+    }
 
     // the next half's copies have landed and every wave is done with this stage
     __syncthreads();
