@@ -120,19 +120,22 @@ struct BwdParams {
 
 // LDS tile of BMB rows x D bf16, row-major and unpadded, filled by direct
 // global -> LDS copies (16 bytes per lane, lane order). Chunk j (16 bytes)
-// of row r sits at chunk position j ^ sw(r), sw(r) = 2 (r % 4) + (r / 4) % 2
-// (+ 8 ((r / 8) % 2) when a row has 16 chunks): any 8 consecutive rows put
-// one chunk on 8 distinct bank groups (row-operand reads, ds_read_b128), and
-// any 4 rows r0..r0+3 (r0 % 4 == 0) put a chunk pair {2m, 2m+1} on 8
-// distinct positions (transposing reads, ds_read_b64_tr_b16).
+// of row r sits at chunk position j ^ sw(r). With 16 chunks a row (one
+// 256-byte bank line), sw(r) = 4 (r % 4) + (r / 4) % 4 is a bijection on any
+// 16 consecutive rows, so the row-operand reads (ds_read_b128: 16 rows, one
+// chunk each per cycle) hit 16 distinct bank groups, and any 4 rows r0..r0+3
+// (r0 % 4 == 0) put 4 adjacent chunks on 16 distinct positions (transposing
+// reads, ds_read_b64_tr_b16: 4 rows x 4 chunks per half-wave). Rows 8 apart
+// differ in chunk bit 1 only (TR8: the byte offset of the +8-row read).
+// With 8 chunks a row, sw(r) = 2 (r % 4) + (r / 4) % 2.
 template <int D>
 struct RowTile {
   static constexpr int CPR = D / 8;                  // 16-byte chunks per row
   static constexpr int ROW = 2 * D;                  // bytes per row
   static constexpr int BYTES = BMB * ROW;
+  static constexpr int TR8 = 32;                     // sw(r + 8) = sw(r) ^ 2 (r % 16 < 8, 16 chunks)
   static __device__ int sw(int r) {
-    const int s = 2 * (r & 3) + ((r >> 2) & 1);
-    return CPR >= 16 ? s + 8 * ((r >> 3) & 1) : s;
+    return CPR >= 16 ? 4 * (r & 3) + ((r >> 2) & 3) : 2 * (r & 3) + ((r >> 2) & 1);
   }
 };
 
@@ -217,8 +220,8 @@ __global__ __launch_bounds__(NTK) void attn_bwd_kv_kernel(BwdParams p) {
   // 16-lane group q, lane s addresses row 4 (q / 2) + s / 4 (+ the step's
   // base, a multiple of 8) and columns 16 (q % 2) + 4 (s % 4) .. +3 of the
   // 32-column block db; it receives the 4 rows of column 16 (q % 2) + s.
-  // The +8-row read of a pair flips chunk bit 3 of the swizzle (rows of 16
-  // chunks only).
+  // The +8-row read of a pair flips chunk bit 1 of the swizzle (byte offset
+  // XOR TR8, rows of 16 chunks only).
   int t_off[D / 32];
   {
     const int q4 = lane >> 4, s16 = lane & 15;
@@ -229,15 +232,6 @@ __global__ __launch_bounds__(NTK) void attn_bwd_kv_kernel(BwdParams p) {
       t_off[db] = row * RT::ROW + 16 * ((col >> 3) ^ RT::sw(row)) + 2 * (col & 7);
     }
   }
-  auto tr_pair = [&](const unsigned char *tile, int base_row, int db) {
-    const unsigned char *a = tile + t_off[db] + base_row * RT::ROW;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a));
-    const unsigned char *b2 = RT::CPR >= 16 ? tile + ((t_off[db] ^ 128) + (base_row + 8) * RT::ROW)
-                                            : a + 8 * RT::ROW;
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(b2));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
-
   // The (Q tile, query head) iterations run in order it * group + hi.
   // Partner entries come through the scalar cache (the index is uniform), so
   // no vector load has to wait behind the in-flight row copies.
@@ -392,7 +386,7 @@ __global__ __launch_bounds__(NTK) void attn_bwd_kv_kernel(BwdParams p) {
       const unsigned cbase = static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_void *)cur));
       auto tr_issue = [&](unsigned tile, int base_row, int db, u32x2 &lo, u32x2 &hi) {
         const unsigned a = tile + t_off[db] + base_row * RT::ROW;
-        const unsigned b2 = RT::CPR >= 16 ? tile + (t_off[db] ^ 128) + (base_row + 8) * RT::ROW : a + 8 * RT::ROW;
+        const unsigned b2 = RT::CPR >= 16 ? tile + (t_off[db] ^ RT::TR8) + (base_row + 8) * RT::ROW : a + 8 * RT::ROW;
         asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a));
         asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hi) : "v"(b2));
       };
@@ -725,7 +719,7 @@ __global__ __launch_bounds__(128 * NH) void attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
           const unsigned a = kbase + t_off[db] + row0 * RT::ROW;
-          const unsigned a8 = RT::CPR >= 16 ? kbase + (t_off[db] ^ 128) + (row0 + 8) * RT::ROW : a + 8 * RT::ROW;
+          const unsigned a8 = RT::CPR >= 16 ? kbase + (t_off[db] ^ RT::TR8) + (row0 + 8) * RT::ROW : a + 8 * RT::ROW;
           asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r[2 * db]) : "v"(a));
           asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r[2 * db + 1]) : "v"(a8));
         }

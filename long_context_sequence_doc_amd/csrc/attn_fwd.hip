@@ -95,10 +95,11 @@ struct Stage {
   // K is read as 16-byte row chunks by 32 consecutive rows: chunk ^ (row % CPR)
   // spreads any run of CPR consecutive rows over distinct chunk positions.
   static __device__ int ksw(int row) { return row % CPR; }
-  // V is read by ds_read_b64_tr_b16: each 16 lanes take 8 bytes from each of
-  // 4 consecutive rows at 2 adjacent chunks; XOR by 2 * (row % 4) moves the
-  // 4 rows' chunk pairs onto distinct banks.
-  static __device__ int vsw(int row) { return 2 * (row % 4); }
+  // V is read by ds_read_b64_tr_b16: each half-wave takes 8 bytes from each
+  // of 4 consecutive rows at 4 adjacent chunks. With 256-byte rows (one bank
+  // line) XOR by 4 * (row % 4) puts the 16 (row, chunk) pairs on distinct
+  // banks; with 128-byte rows two rows share a line and 2 * (row % 4) does.
+  static __device__ int vsw(int row) { return CPR >= 16 ? 4 * (row % 4) : 2 * (row % 4); }
 };
 
 // Per-thread element offsets (from the tile's first row of the KV head) of
