@@ -379,7 +379,7 @@ def main():
             "useful_pairs_per_head": rf.useful_pairs_per_head,
             "useful_flop_per_step": flop,
             "flop_per_pair_per_head": (14 if headline_bwd else 4) * w.d,
-            "tiles": {"forward": [128, 64], "backward": [64, 128]},
+            "tiles": {"forward": [rf.block_m, 64], "backward": [64, 128]},
             "plan_host_s": round(plan_s, 3),
         },
         "roofline": {

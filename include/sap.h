@@ -105,8 +105,10 @@ typedef struct {
  *   ranges pairwise disjoint and local ranges pairwise disjoint within a
  *   table. n_kv_segs may be 0 (an empty call).
  * block_m, block_n: one of 16, 32, 64, 128, 256. Compute calls accept only
- *   the shapes they are compiled for: forward 128 x 64 (block_m x block_n),
- *   backward 64 x 128; merge accepts any plan.
+ *   the shapes they are compiled for: forward 128 x 64 or 256 x 64
+ *   (block_m x block_n; 256-row tiles let the 8 waves of a workgroup share
+ *   each K/V tile when the GQA group size is odd), backward 64 x 128; merge
+ *   accepts any plan.
  * out: receives the plan; release with sap_plan_free.
  * Errors: SAP_ERR_INVALID_ARG, SAP_ERR_NO_MEMORY.
  */
@@ -170,7 +172,8 @@ sap_status sap_balance(const int32_t *cu_seqlens, int32_t n_docs, int32_t n_rank
  * O = 0, LSE = -inf); all other rows are left untouched.
  * q, k, v: bf16 device pointers to local row 0 of each buffer.
  * hq % hkv == 0; d in {64, 128}; scale > 0 (usually 1/sqrt(d)).
- * Plan tile shape must be 128 x 64. Deterministic (no atomics).
+ * Plan tile shape must be 128 x 64 or 256 x 64 (same results). Deterministic
+ * (no atomics).
  */
 sap_status sap_attn_fwd(sap_plan_t plan, const void *q, const void *k, const void *v,
                         int64_t q_row_stride, int64_t kv_row_stride,

@@ -8,10 +8,12 @@
 // natural-log log-sum-exp so partial results over disjoint KV sets merge
 // exactly.
 //
-// Layout of the work (one workgroup = one 128-row Q tile x NH query heads of
-// one KV head; NH = 2 when the GQA group size is even, else 1):
-//   * 4 waves per head, each owns 32 query rows of the tile; the heads'
-//     waves share every staged K / V tile.
+// Layout of the work (one workgroup = one Q tile of the plan x NH query heads
+// of one KV head: 128-row tiles with NH = 2 when the GQA group size is even,
+// else 1; 256-row tiles with NH = 1):
+//   * one wave per 32 query rows of the tile and head; all the workgroup's
+//     waves (8, or 4 for 128-row tiles of an odd group) share every staged
+//     K / V tile.
 //   * Per 64-key KV tile: S^T = K Q^T with v_mfma_f32_32x32x16_bf16. In the
 //     32x32 accumulator a lane holds one column (= one query) and 16 rows (=
 //     keys), so a query's scores sit in one lane pair (lane, lane ^ 32): row
@@ -57,16 +59,12 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void global_void;
 
-constexpr int BM = 128;
 constexpr int BN = 64;
-constexpr int NWAVES = 4;                 // waves per query head
-constexpr int NTHREADS = 64 * NWAVES;
 constexpr int NXCD = 8;
 constexpr float LOG2E = 1.4426950408889634f;
 // running max moves only when the new max exceeds it by more than this many
 // powers of two (p = 2^(s*c - m*c) then stays <= 2^8)
 constexpr float RESCALE_LOG2 = 8.0f;
-static_assert(NWAVES * 32 == BM, "one 32-row slice of the Q tile per wave");
 
 struct FwdParams {
   const unsigned short *q, *k, *v;
@@ -162,9 +160,13 @@ __device__ inline unsigned pack_bf16(float lo, float hi) {
 // MERGE: o / lse hold a running result that this call's partial is merged
 // into (the ring step's merge folded into the epilogue), instead of being
 // overwritten.
-template <int D, bool MERGE, int NH>
-__global__ __launch_bounds__(NTHREADS * NH) void attn_fwd_kernel(FwdParams p) {
-  constexpr int NT = NTHREADS * NH;
+// TM: rows of the plan's Q tiles (128 or 256), one 32-row slice per wave;
+// NH: query heads per workgroup (2 only with TM = 128).
+template <int D, bool MERGE, int TM, int NH>
+__global__ __launch_bounds__(2 * TM * NH) void attn_fwd_kernel(FwdParams p) {
+  constexpr int WPH = TM / 32;                    // waves per query head
+  constexpr int NT = 64 * WPH * NH;
+  static_assert(NH == 1 || TM == 128, "two heads per workgroup only with 128-row tiles");
   using ST = Stage<D, NT>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * ST::BYTES];
 
@@ -175,14 +177,14 @@ __global__ __launch_bounds__(NTHREADS * NH) void attn_fwd_kernel(FwdParams p) {
   const int G = (slot / pairs) * NXCD + xcd;
   if (G >= p.n_groups) return;
   const int w = G / p.hkv, g = G % p.hkv;
-  const int h = g * p.group + (slot % pairs) * NH + (threadIdx.x >> 8);
+  const int h = g * p.group + (slot % pairs) * NH + (int(threadIdx.x) >> 6) / WPH;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const WorkItem wi = p.work[w];
   const WorkRange rg = p.range[w];
 
-  const int my_row = (wave & 3) * 32 + l32;       // row within the Q tile
+  const int my_row = (wave % WPH) * 32 + l32;     // row within the Q tile
   const bool row_ok = my_row < wi.n;
   const int qg = wi.global_start + my_row;        // global position of this lane's query
   const int dsq = row_ok ? p.ds_q[wi.local_start + my_row] : 0;
@@ -397,20 +399,31 @@ hipError_t launch_attn_fwd(const FwdLaunch &a, hipStream_t stream) {
   p.n_groups = a.n_work * a.hkv;
   p.scale = a.scale;
   p.c = a.scale * LOG2E;
-  const int nh = p.group % 2 == 0 ? 2 : 1;         // query heads per workgroup
+  // 128-row tiles: two query heads per workgroup when the GQA group is even;
+  // 256-row tiles: one head, its 8 waves over the tile's rows. Either way
+  // 8 waves share each staged K / V tile (4 for 128-row tiles, odd groups).
+  const int tm = a.block_m;
+  const int nh = tm == 128 && p.group % 2 == 0 ? 2 : 1;   // query heads per workgroup
   const int64_t slots = (int64_t(p.n_groups) + NXCD - 1) / NXCD;
   const int64_t blocks = slots * NXCD * (p.group / nh);
   // 32-bit row offsets inside a 64-row tile
   if (blocks > INT32_MAX || a.kv_row_stride > INT32_MAX / BN) return hipErrorInvalidValue;
-  const dim3 grid{static_cast<unsigned>(blocks)}, block{static_cast<unsigned>(NTHREADS * nh)};
-#define SAP_FWD_LAUNCH(DD, MM, HH) hipLaunchKernelGGL((attn_fwd_kernel<DD, MM, HH>), grid, block, 0, stream, p)
+  if (tm != 128 && tm != 256) return hipErrorInvalidValue;
+  const dim3 grid{static_cast<unsigned>(blocks)}, block{static_cast<unsigned>(2 * tm * nh)};
+#define SAP_FWD_LAUNCH(DD, MM, TT, HH) \
+  hipLaunchKernelGGL((attn_fwd_kernel<DD, MM, TT, HH>), grid, block, 0, stream, p)
+#define SAP_FWD_SHAPES(DD, MM)                                   \
+  do {                                                           \
+    if (tm == 256) SAP_FWD_LAUNCH(DD, MM, 256, 1);               \
+    else if (nh == 2) SAP_FWD_LAUNCH(DD, MM, 128, 2);            \
+    else SAP_FWD_LAUNCH(DD, MM, 128, 1);                         \
+  } while (0)
   if (a.d == 128) {
-    if (nh == 2) { if (a.merge) SAP_FWD_LAUNCH(128, true, 2); else SAP_FWD_LAUNCH(128, false, 2); }
-    else { if (a.merge) SAP_FWD_LAUNCH(128, true, 1); else SAP_FWD_LAUNCH(128, false, 1); }
+    if (a.merge) SAP_FWD_SHAPES(128, true); else SAP_FWD_SHAPES(128, false);
   } else {
-    if (nh == 2) { if (a.merge) SAP_FWD_LAUNCH(64, true, 2); else SAP_FWD_LAUNCH(64, false, 2); }
-    else { if (a.merge) SAP_FWD_LAUNCH(64, true, 1); else SAP_FWD_LAUNCH(64, false, 1); }
+    if (a.merge) SAP_FWD_SHAPES(64, true); else SAP_FWD_SHAPES(64, false);
   }
+#undef SAP_FWD_SHAPES
 #undef SAP_FWD_LAUNCH
   return hipGetLastError();
 }

@@ -21,6 +21,7 @@ struct FwdLaunch {
   const PartnerEntry *partners;
   const int32_t *ds_q;
   int32_t n_work;
+  int32_t block_m;    // Q tile rows of the plan: 128 or 256
   bool merge;         // o / lse are a running result to merge into
 };
 

@@ -231,7 +231,8 @@ sap_status fwd_impl(sap_plan_t plan, const void *q, const void *k, const void *v
   sap_status s = check_heads(hq, hkv, d);
   if (s != SAP_OK) return s;
   const sap::Plan &P = plan->p;
-  if (P.bm != 128 || P.bn != 64) return fail(SAP_ERR_UNSUPPORTED, "forward needs a 128 x 64 plan");
+  if ((P.bm != 128 && P.bm != 256) || P.bn != 64)
+    return fail(SAP_ERR_UNSUPPORTED, "forward needs a 128 x 64 or 256 x 64 plan");
   if (!(scale > 0.f) || !(scale < 1e30f)) return fail(SAP_ERR_INVALID_ARG, "scale must be positive and finite");
   if (P.q_work.empty()) return ok();
   if ((s = check_uploaded(plan)) != SAP_OK) return s;
@@ -247,6 +248,7 @@ sap_status fwd_impl(sap_plan_t plan, const void *q, const void *k, const void *v
   a.o = o; a.lse = lse; a.tq = P.tq;
   a.work = P.dev.q_work; a.range = P.dev.q_range; a.partners = P.dev.q_partners; a.ds_q = P.dev.ds_q;
   a.n_work = int32_t(P.q_work.size());
+  a.block_m = P.bm;
   a.merge = merge;
   hipError_t e = sap::launch_attn_fwd(a, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");

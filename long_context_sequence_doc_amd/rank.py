@@ -39,15 +39,29 @@ from . import (sap_attn_bwd_accumulate, sap_attn_bwd_rowterm, sap_attn_bwd_works
                sap_plan_upload)
 
 BLOCK_M, BLOCK_N = 128, 64
+N_CU = 256
+
+
+def forward_block_m(q_segs, hq: int, hkv: int) -> int:
+    """Q tile height of the forward plans: 256 when the GQA group is odd (a
+    workgroup then holds one head, and 256-row tiles let 8 waves share each
+    staged K / V tile instead of 4) and the rank has rows enough for about
+    four such workgroups per compute unit; else 128 (even groups pair two
+    heads per workgroup instead)."""
+    tq = max(ls + ge - gs for gs, ge, ls in q_segs)
+    if (hq // hkv) % 2 == 1 and (tq // 256) * hq >= 4 * N_CU:
+        return 256
+    return BLOCK_M
 
 
 class RankForward:
     def __init__(self, cu_seqlens, q_segs: Sequence[Tuple[int, int, int]],
                  step_kv_segs: List[Sequence[Tuple[int, int, int]]], hq: int, hkv: int, d: int,
-                 scale: float, device: str = "cuda", fused_merge: bool = True):
+                 scale: float, device: str = "cuda", fused_merge: bool = True, block_m: int = 0):
         self.hq, self.hkv, self.d, self.scale = hq, hkv, d, scale
         self.fused_merge = fused_merge
-        self.plans = [sap_plan(cu_seqlens, q_segs, kv, BLOCK_M, BLOCK_N) for kv in step_kv_segs]
+        self.block_m = block_m or forward_block_m(q_segs, hq, hkv)
+        self.plans = [sap_plan(cu_seqlens, q_segs, kv, self.block_m, BLOCK_N) for kv in step_kv_segs]
         self.infos = [sap_plan_info(p) for p in self.plans]
         first = self.infos[0]
         if first["n_touched_q_tiles"] != first["n_q_tiles"]:
@@ -107,12 +121,12 @@ class RankForward:
 
     @classmethod
     def concatenated(cls, cu_seqlens, q_segs, step_kv_segs, hq: int, hkv: int, d: int, scale: float,
-                     device: str = "cuda"):
+                     device: str = "cuda", block_m: int = 0):
         """One forward call over every step's KV segments together (the steps
         must address disjoint KV rows): the fused ring pass for a rank whose KV
         chunks are all resident."""
         union = [seg for segs in step_kv_segs for seg in segs]
-        return cls(cu_seqlens, q_segs, [union], hq, hkv, d, scale, device)
+        return cls(cu_seqlens, q_segs, [union], hq, hkv, d, scale, device, block_m=block_m)
 
 
 class RankBackward:

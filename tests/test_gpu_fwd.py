@@ -63,10 +63,12 @@ def test_tiny_full_sequence():
     say(f"  tiny vs fp32-input oracle (not gated): max|dO|={np.abs(o - fo).max():.3e}")
 
 
+@pytest.mark.parametrize("block_m", [128, 256])
 @pytest.mark.parametrize("seed", range(10))
-def test_random_small_layouts(seed):
+def test_random_small_layouts(seed, block_m):
     """Ragged tiles, 1-token and empty documents, GQA, D in {64, 128},
-    non-contiguous segments, strided Q rows; untouched rows stay NaN."""
+    non-contiguous segments, strided Q rows, 128- and 256-row Q tiles;
+    untouched rows stay NaN."""
     sap = _sap()
     rng = np.random.default_rng(900 + seed)
     d = 128 if seed % 2 else 64
@@ -81,7 +83,8 @@ def test_random_small_layouts(seed):
     q_segs = [s for s in q_segs if s[1] > s[0]]
     c0 = int(rng.integers(0, total))
     kv_segs = [(c0, total, 0), (0, c0, total - c0 + 7)] if c0 > 0 else [(0, total, 0)]
-    say(f"case random seed={seed} total={total} docs={len(lengths)} hq={hq} hkv={hkv} d={d} q={q_segs} kv={kv_segs}")
+    say(f"case random seed={seed} block_m={block_m} total={total} docs={len(lengths)} hq={hq} hkv={hkv} d={d} "
+        f"q={q_segs} kv={kv_segs}")
     gq = _globals(q_segs, max(ls + ge - gs for gs, ge, ls in q_segs))
     gk = _globals(kv_segs, max(ls + ge - gs for gs, ge, ls in kv_segs))
     rs = np.random.default_rng(seed)
@@ -95,7 +98,7 @@ def test_random_small_layouts(seed):
     vl = np.zeros((len(gk), hkv, d), dtype=np.uint16)
     kl[gk >= 0], vl[gk >= 0] = kf[gk[gk >= 0]], vf[gk[gk >= 0]]
     import torch
-    plan = sap.sap_plan(cu, q_segs, kv_segs, 128, 64)
+    plan = sap.sap_plan(cu, q_segs, kv_segs, block_m, 64)
     info = sap.sap_plan_info(plan)
     qd, kd, vd = to_dev(ql), to_dev(kl), to_dev(vl)
     o = torch.full((info["tq"], hq, d), float("nan"), device="cuda")
@@ -114,7 +117,7 @@ def test_random_small_layouts(seed):
     q64[valid] = f64(qf[gq[valid]])
     ro, rl = A.forward(q64, f64(kl), f64(vl), np.where(gq >= 0, gq, 0), np.where(gk >= 0, gk, -10**9), cu,
                        1.0 / np.sqrt(d), rows=rows)
-    compare(o, lse, ro, rl, rows=rows, label=f"random{seed}")
+    compare(o, lse, ro, rl, rows=rows, label=f"random{seed}/{block_m}")
 
 
 def test_forward_is_deterministic():
@@ -196,8 +199,9 @@ def test_ring_rank_single_call():
     rc.close()
 
 
+@pytest.mark.parametrize("block_m", [128, 256])
 @pytest.mark.parametrize("seed", range(4))
-def test_fused_merge_random(seed):
+def test_fused_merge_random(seed, block_m):
     """sap_attn_fwd over KV part A, then sap_attn_fwd_merge over part B, against
     the oracle over A and B together. Rows of touched tiles with no key in B
     keep their values exactly; rows with no key in A (LSE -inf) take B's."""
@@ -218,9 +222,10 @@ def test_fused_merge_random(seed):
     if seed % 2:
         segs_a, segs_b = segs_b, segs_a
     q_segs = [(0, total, 0)]
-    say(f"case fused merge seed {seed}: T={total} docs={len(lengths)} cut={cut} hq={hq} hkv={hkv} d={d}")
-    pa = sap.sap_plan(cu, q_segs, segs_a, 128, 64)
-    pb = sap.sap_plan(cu, q_segs, segs_b, 128, 64)
+    say(f"case fused merge seed {seed} block_m {block_m}: T={total} docs={len(lengths)} cut={cut} hq={hq} "
+        f"hkv={hkv} d={d}")
+    pa = sap.sap_plan(cu, q_segs, segs_a, block_m, 64)
+    pb = sap.sap_plan(cu, q_segs, segs_b, block_m, 64)
     q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
     o = torch.zeros((total, hq, d), device="cuda")
     lse = torch.full((hq, total), float("-inf"), device="cuda")
@@ -234,7 +239,7 @@ def test_fused_merge_random(seed):
     torch.cuda.synchronize()
     g = np.arange(total)
     ro, rl = A.forward(f64(qb), f64(kb), f64(vb), g, g, cu, scale)
-    compare(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, label=f"fused merge seed {seed}")
+    compare(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, label=f"fused merge seed {seed}/{block_m}")
     # rows with no key in B: unchanged, bit for bit
     gb = np.concatenate([np.arange(a, b) for a, b, _ in segs_b])
     _, rl_b = A.forward(f64(qb), f64(kb[gb]), f64(vb[gb]), g, gb, cu, scale)

@@ -29,7 +29,7 @@ def _compare(cu, q_segs, kv_segs, bm, bn):
 
 
 @pytest.mark.parametrize("name", ["tiny", "ring", "zigzag", "train", "ulysses"])
-@pytest.mark.parametrize("shape", [(128, 64), (64, 128)])
+@pytest.mark.parametrize("shape", [(128, 64), (64, 128), (256, 64)])
 def test_workloads_exact(name, shape):
     w = W.by_name(name)
     if name == "ulysses" and shape != (128, 64):
