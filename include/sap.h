@@ -187,8 +187,8 @@ sap_status sap_attn_fwd(sap_plan_t plan, const void *q, const void *k, const voi
  * (fp32 device, in place) exactly as sap_lse_merge does,
  *   L = ln(e^La + e^Lb);  O = e^(La-L) O_a + e^(Lb-L) O_b,
  * for the rows of touched Q tiles that have at least one allowed key in this
- * call; every other row keeps its running values. Same tile shape (128 x 64),
- * arguments and checks as sap_attn_fwd. A ring rank calls sap_attn_fwd for
+ * call; every other row keeps its running values. Same tile shapes
+ * (128 x 64 or 256 x 64), arguments and checks as sap_attn_fwd. A ring rank calls sap_attn_fwd for
  * its first step and sap_attn_fwd_merge for each later step: no partial
  * buffers, no separate merge pass. Deterministic (no atomics).
  */
