@@ -685,27 +685,39 @@ __global__ __launch_bounds__(128 * NH) void attn_bwd_dq_kernel(BwdParams p) {
     }
     const int hi_r = hi - 4 * hf, lo_r = lo - 4 * hf;
     bf16x8 sb[KBQ][2];
+    // FULL, complete tiles take the path without the per-pair mask (the
+    // condition is uniform over the workgroup); with two heads the second
+    // path would push the kernel past 256 registers, so it always masks
+    auto ds_t = [&](auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-    for (int kb = 0; kb < KBQ; ++kb)
+      for (int kb = 0; kb < KBQ; ++kb)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float sv[8];
+        for (int u = 0; u < 2; ++u) {
+          float sv[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int i = 8 * u + j;
-          float x = __builtin_fmaf(sacc[kb][i], c, -lse2);
-          const int kc = kb * 32 + 8 * (i >> 2) + (i & 3);
-          x = (kc <= hi_r && kc >= lo_r) ? x : -INFINITY;    // masked pairs: exp2(-inf) = 0
-          const float pr = __builtin_amdgcn_exp2f(x);
-          sv[j] = pr * (pacc[kb][i] - dlt);
+          for (int j = 0; j < 8; ++j) {
+            const int i = 8 * u + j;
+            float x = __builtin_fmaf(sacc[kb][i], c, -lse2);
+            if (MASK) {
+              const int kc = kb * 32 + 8 * (i >> 2) + (i & 3);
+              x = (kc <= hi_r && kc >= lo_r) ? x : -INFINITY;    // masked pairs: exp2(-inf) = 0
+            }
+            const float pr = __builtin_amdgcn_exp2f(x);
+            sv[j] = pr * (pacc[kb][i] - dlt);
+          }
+          u32x4 sk;
+          sk.x = pack_bf16(sv[0], sv[1]);
+          sk.y = pack_bf16(sv[2], sv[3]);
+          sk.z = pack_bf16(sv[4], sv[5]);
+          sk.w = pack_bf16(sv[6], sv[7]);
+          sb[kb][u] = as_bf16x8(sk);
         }
-        u32x4 sk;
-        sk.x = pack_bf16(sv[0], sv[1]);
-        sk.y = pack_bf16(sv[2], sv[3]);
-        sk.z = pack_bf16(sv[4], sv[5]);
-        sk.w = pack_bf16(sv[6], sv[7]);
-        sb[kb][u] = as_bf16x8(sk);
-      }
+    };
+    if (NH == 2 || masked)
+      ds_t(std::true_type{});
+    else
+      ds_t(std::false_type{});
 
     // ---- dQ^T += K^T dS^T (k = 16 keys per step: kb*32 + 16u + 4hf + (0..3 | 8..11)).
     //      The transposing reads go through inline asm with explicit waits:
