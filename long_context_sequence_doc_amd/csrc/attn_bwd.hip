@@ -71,6 +71,16 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 __device__ inline bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
+// (the index can then feed immediate instruction operands)
+template <int N, int I = 0, class F>
+__device__ inline void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
 __device__ inline unsigned pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
@@ -232,6 +242,15 @@ __global__ __launch_bounds__(NTK) void attn_bwd_kv_kernel(BwdParams p) {
       t_off[db] = row * RT::ROW + 16 * ((col >> 3) ^ RT::sw(row)) + 2 * (col & 7);
     }
   }
+  // per-lane transposing-read offsets of this wave's row block: rows
+  // qb*32 + (0..7) and, for the second read of a pair, + 8
+  int t_lo[D / 32], t_hi[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    t_lo[db] = t_off[db] + qb * 32 * RT::ROW;
+    t_hi[db] = (RT::CPR >= 16 ? (t_off[db] ^ RT::TR8) : t_off[db]) + (qb * 32 + 8) * RT::ROW;
+  }
+
   // The (Q tile, query head) iterations run in order it * group + hi.
   // Partner entries come through the scalar cache (the index is uniform), so
   // no vector load has to wait behind the in-flight row copies.
@@ -383,34 +402,40 @@ __global__ __launch_bounds__(NTK) void attn_bwd_kv_kernel(BwdParams p) {
     //      the compiler cannot tell them apart from the in-flight copies into
     //      the other stage and would wait for those first.
     {
+      // one address per 32-column block and read of a pair; the tile (dO or
+      // Q) and the 16-row step go into the instructions' immediate offsets
       const unsigned cbase = static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_void *)cur));
-      auto tr_issue = [&](unsigned tile, int base_row, int db, u32x2 &lo, u32x2 &hi) {
-        const unsigned a = tile + t_off[db] + base_row * RT::ROW;
-        const unsigned b2 = RT::CPR >= 16 ? tile + (t_off[db] ^ RT::TR8) + (base_row + 8) * RT::ROW : a + 8 * RT::ROW;
-        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a));
-        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hi) : "v"(b2));
-      };
-      auto issue = [&](int k, u32x2 (&r)[4]) {
-        const int u = k / (D / 32), db = k % (D / 32);
-        tr_issue(cbase + KS::DO, qb * 32 + 16 * u, db, r[0], r[1]);
-        tr_issue(cbase + KS::Q, qb * 32 + 16 * u, db, r[2], r[3]);
+      unsigned a_lo[D / 32], a_hi[D / 32];
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        a_lo[db] = cbase + t_lo[db];
+        a_hi[db] = cbase + t_hi[db];
+      }
+      auto issue = [](auto kc, const unsigned (&lo)[D / 32], const unsigned (&hi)[D / 32], u32x2 (&r)[4]) {
+        constexpr int k = decltype(kc)::value;
+        constexpr int u = k / (D / 32), db = k % (D / 32);
+        constexpr int odo = KS::DO + 16 * u * RT::ROW, oq = KS::Q + 16 * u * RT::ROW;
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r[0]) : "v"(lo[db]), "n"(odo));
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r[1]) : "v"(hi[db]), "n"(odo));
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r[2]) : "v"(lo[db]), "n"(oq));
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r[3]) : "v"(hi[db]), "n"(oq));
       };
       auto join = [](const u32x2 &lo, const u32x2 &hi) { return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y}); };
       u32x2 rr[2][4];
-      issue(0, rr[0]);
-#pragma unroll
-      for (int k = 0; k < 2 * (D / 32); ++k) {
-        const int u = k / (D / 32), db = k % (D / 32);
+      issue(std::integral_constant<int, 0>{}, a_lo, a_hi, rr[0]);
+      static_for<2 * (D / 32)>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        constexpr int u = k / (D / 32), db = k % (D / 32);
         u32x2 (&r)[4] = rr[k & 1];
-        if (k + 1 < 2 * (D / 32)) {
-          issue(k + 1, rr[(k + 1) & 1]);
+        if constexpr (k + 1 < 2 * (D / 32)) {
+          issue(std::integral_constant<int, k + 1>{}, a_lo, a_hi, rr[(k + 1) & 1]);
           asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
         } else {
           asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
         }
         dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(r[0], r[1]), pb[u], dva[db], 0, 0, 0);
         dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(r[2], r[3]), sb[u], dka[db], 0, 0, 0);
-      }
+      });
     }
 
     // the next iteration's row terms (loaded above, latency hidden by the math)
@@ -725,24 +750,30 @@ __global__ __launch_bounds__(128 * NH) void attn_bwd_dq_kernel(BwdParams p) {
     //      the other stage and would wait for those first.
     {
       constexpr int NSTEP = 2 * KBQ, NR = 2 * (D / 32);
+      // one address per 32-column block and read of a pair; the 16-key step
+      // goes into the instructions' immediate offsets
       const unsigned kbase = static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_void *)(cur + KOFF)));
-      auto issue = [&](int st, u32x2 (&r)[NR]) {
-        const int row0 = 16 * st;                 // kb * 32 + 16 u
+      unsigned a_lo[D / 32], a_hi[D / 32];
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        a_lo[db] = kbase + t_off[db];
+        a_hi[db] = kbase + (RT::CPR >= 16 ? (t_off[db] ^ RT::TR8) : t_off[db]) + 8 * RT::ROW;
+      }
+      auto issue = [](auto sc, const unsigned (&lo)[D / 32], const unsigned (&hi)[D / 32], u32x2 (&r)[NR]) {
+        constexpr int off = 16 * decltype(sc)::value * RT::ROW;   // kb * 32 + 16 u rows
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const unsigned a = kbase + t_off[db] + row0 * RT::ROW;
-          const unsigned a8 = RT::CPR >= 16 ? kbase + (t_off[db] ^ RT::TR8) + (row0 + 8) * RT::ROW : a + 8 * RT::ROW;
-          asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r[2 * db]) : "v"(a));
-          asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r[2 * db + 1]) : "v"(a8));
+          asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r[2 * db]) : "v"(lo[db]), "n"(off));
+          asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r[2 * db + 1]) : "v"(hi[db]), "n"(off));
         }
       };
       u32x2 rr[2][NR];
-      issue(0, rr[0]);
-#pragma unroll
-      for (int st = 0; st < NSTEP; ++st) {
+      issue(std::integral_constant<int, 0>{}, a_lo, a_hi, rr[0]);
+      static_for<NSTEP>([&](auto stc) {
+        constexpr int st = decltype(stc)::value;
         u32x2 (&r)[NR] = rr[st & 1];
-        if (st + 1 < NSTEP) {
-          issue(st + 1, rr[(st + 1) & 1]);
+        if constexpr (st + 1 < NSTEP) {
+          issue(std::integral_constant<int, st + 1>{}, a_lo, a_hi, rr[(st + 1) & 1]);
           if constexpr (NR == 8)
             asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]),
                          "+v"(r[5]), "+v"(r[6]), "+v"(r[7]));
@@ -755,13 +786,13 @@ __global__ __launch_bounds__(128 * NH) void attn_bwd_dq_kernel(BwdParams p) {
           else
             asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
         }
-        const int kb = st >> 1, u = st & 1;
+        constexpr int kb = st >> 1, u = st & 1;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
           const bf16x8 ak = as_bf16x8(u32x4{r[2 * db].x, r[2 * db].y, r[2 * db + 1].x, r[2 * db + 1].y});
           qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, sb[kb][u], qacc[db], 0, 0, 0);
         }
-      }
+      });
     }
 
     // the next half's copies have landed and every wave is done with this stage
