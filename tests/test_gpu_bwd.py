@@ -199,20 +199,18 @@ def test_training_fwd_bwd_sampled():
     rf.close()
 
 
-def test_zigzag_rank_fwd_bwd_sampled():
-    """The benchmarked configuration: 128K zigzag GQA rank 3, forward over the
-    ring steps with merges, row terms once, backward per non-empty step;
-    sampled dQ rows and dK/dV rows against the oracle's own forward/backward."""
-    _sap()
+def _rank_fwd_bwd_sampled(w, label, active=None):
+    """Forward over the ring steps with merges, row terms once, backward per
+    non-empty step; sampled dQ rows and dK/dV rows of KV head 0 against the
+    oracle's own forward/backward."""
     import torch
     from long_context_sequence_doc_amd.rank import RankBackward, RankForward
-    w = W.zigzag_rank(3)
     t = tensors("zigzag", True)
-    say("case zigzag_sp8_128k_gqa_rank3 fwd+bwd (ring steps), sampled rows")
     steps = [s.kv_segs for s in w.steps]
     rf = RankForward(w.cu, w.q_segs, steps, w.hq, w.hkv, w.d, w.scale)
     rb = RankBackward(w.cu, w.q_segs, steps, w.hq, w.hkv, w.d, w.scale)
-    assert rb.active == [0, 1, 7]
+    if active is not None:
+        assert rb.active == active
     ql, dol = W.local_rows(t.q, w.q_segs), W.local_rows(t.do, w.q_segs)
     qd, dod, kd, vd = to_dev(ql), to_dev(dol), to_dev(t.k), to_dev(t.v)
     o, lse = rf.run(qd, kd, vd, qd.stride(0), kd.stride(0))
@@ -238,8 +236,8 @@ def test_zigzag_rank_fwd_bwd_sampled():
     o_r, lse_r = A.forward(q64, k64, v64, gq[rows], allk, cu, w.scale)
     dq_ref, _, _ = A.backward(q64, k64, v64, do64, o_r, lse_r, gq[rows], allk, cu, w.scale,
                               cols=np.zeros(0, dtype=np.int64))
-    _check("dQ zigzag", dq.cpu().numpy()[rows], dq_ref)
-    # (b) dK / dV of KV head 0 (query heads 0..3) on keys sampled from every
+    _check(f"dQ {label}", dq.cpu().numpy()[rows], dq_ref)
+    # (b) dK / dV of KV head 0 (its query heads) on keys sampled from every
     #     non-empty step's chunks: the oracle forward on all rows of those heads
     grp = w.hq // w.hkv
     cols = set()
@@ -255,7 +253,27 @@ def test_zigzag_rank_fwd_bwd_sampled():
     o_h, lse_h = A.forward(qh, kh, vh, gq, allk, cu, w.scale)
     _, dk_ref, dv_ref = A.backward(qh, kh, vh, doh, o_h, lse_h, gq, allk, cu, w.scale,
                                    rows=np.zeros(0, dtype=np.int64), cols=cols)
-    _check("dK zigzag (KV head 0)", dk.cpu().numpy()[:, :1], dk_ref, cols)
-    _check("dV zigzag (KV head 0)", dv.cpu().numpy()[:, :1], dv_ref, cols)
+    _check(f"dK {label} (KV head 0)", dk.cpu().numpy()[:, :1], dk_ref, cols)
+    _check(f"dV {label} (KV head 0)", dv.cpu().numpy()[:, :1], dv_ref, cols)
     rf.close()
     rb.close()
+
+
+def test_zigzag_rank_fwd_bwd_sampled():
+    """The benchmarked configuration: 128K zigzag GQA rank 3 (ring steps 0, 1, 7)."""
+    _sap()
+    say("case zigzag_sp8_128k_gqa_rank3 fwd+bwd (ring steps), sampled rows")
+    _rank_fwd_bwd_sampled(W.zigzag_rank(3), "zigzag", active=[0, 1, 7])
+
+
+def test_balanced_rank_fwd_bwd_sampled():
+    """The same 128K sequence in the document-aware balanced layout (1024-row
+    chunks from sap_balance), rank 3: scattered Q chunks, all 8 ring steps."""
+    sap = _sap()
+    from oracle import balance as B
+    z = W.zigzag_rank(3)
+    owner, _ = sap.sap_balance(z.cu, 8, 1024)
+    assert owner.tolist() == B.balance(z.cu, 8, 1024)[0]
+    w = W.owner_rank(z, owner.tolist(), 3, 1024, "balanced")
+    say(f"case balanced_sp8_128k_gqa_rank3 fwd+bwd ({len(w.q_segs)} Q segments), sampled rows")
+    _rank_fwd_bwd_sampled(w, "balanced")
