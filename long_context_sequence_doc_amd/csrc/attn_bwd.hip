@@ -685,115 +685,108 @@ __global__ __launch_bounds__(128 * NH) void attn_bwd_dq_kernel(BwdParams p) {
     const int k0 = half * HKQ;                    // first key of this part within the tile
     const int kn = min(HKQ, kt.n - k0);           // keys in this part
 
-    // ---- S^T = K Q^T, dP^T = V dO^T (64 keys x this wave's 32 queries)
-    f32x16 sacc[KBQ], pacc[KBQ];
-#pragma unroll
-    for (int kb = 0; kb < KBQ; ++kb) sacc[kb] = pacc[kb] = f32x16{};
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t)
-#pragma unroll
-      for (int kb = 0; kb < KBQ; ++kb) {
-        const int off = kb * 32 * RT::ROW + (r_off ^ (32 * t));
-        const bf16x8 ak = as_bf16x8(*reinterpret_cast<const u32x4 *>(cur + KOFF + off));
-        const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(cur + VOFF + off));
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[t], sacc[kb], 0, 0, 0);
-        pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[t], pacc[kb], 0, 0, 0);
-      }
-
-    // ---- dS^T = P^T o (dP^T - D); element i of key block kb is key
-    //      k0 + kb*32 + 8*(i/4) + 4*hf + (i%4) of the tile
+    // The stage's keys go in 32-key blocks, each through S^T / dP^T, dS^T and
+    // its dQ^T steps before the next, so only one block's score
+    // accumulators are live (room for the unmasked path of FULL tiles).
     const bool masked = kt.cls != SAP_TILE_FULL || kn < HKQ || qt.n < BMB;
-    int lo = -(1 << 30), hi = kn - 1;             // allowed half-local key range of this query
+    int lo = -(1 << 30), hi = kn - 1;             // allowed stage-local key range of this query
     if (masked) {
       if (kt.cls != SAP_TILE_FULL) hi = min(hi, qg - (kt.global_start + k0));
       if (kt.cls == SAP_TILE_PARTIAL) lo = dsq - (kt.global_start + k0);
     }
     const int hi_r = hi - 4 * hf, lo_r = lo - 4 * hf;
-    bf16x8 sb[KBQ][2];
-    // FULL, complete tiles take the path without the per-pair mask (the
-    // condition is uniform over the workgroup); with two heads the second
-    // path would push the kernel past 256 registers, so it always masks
-    auto ds_t = [&](auto mask_tag) {
-      constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int NR = 2 * (D / 32);
+    // transposing reads of K^T: one address per 32-column block and read of
+    // a pair, the 16-key step in the instructions' immediate offsets; inline
+    // asm with explicit waits (the compiler cannot tell them apart from the
+    // in-flight copies into the other stage and would wait for those first)
+    const unsigned kbase = static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_void *)(cur + KOFF)));
+    unsigned a_lo[D / 32], a_hi[D / 32];
 #pragma unroll
-      for (int kb = 0; kb < KBQ; ++kb)
+    for (int db = 0; db < D / 32; ++db) {
+      a_lo[db] = kbase + t_off[db];
+      a_hi[db] = kbase + (RT::CPR >= 16 ? (t_off[db] ^ RT::TR8) : t_off[db]) + 8 * RT::ROW;
+    }
+    auto issue = [](auto sc, const unsigned (&lo_)[D / 32], const unsigned (&hi_)[D / 32], u32x2 (&r)[NR]) {
+      constexpr int off = 16 * decltype(sc)::value * RT::ROW;   // kb * 32 + 16 u rows
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r[2 * db]) : "v"(lo_[db]), "n"(off));
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r[2 * db + 1]) : "v"(hi_[db]), "n"(off));
+      }
+    };
+    auto wait_reads = [](auto keep, u32x2 (&r)[NR]) {
+      if constexpr (decltype(keep)::value) {
+        if constexpr (NR == 8)
+          asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]),
+                       "+v"(r[5]), "+v"(r[6]), "+v"(r[7]));
+        else
+          asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
+      } else {
+        if constexpr (NR == 8)
+          asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]),
+                       "+v"(r[5]), "+v"(r[6]), "+v"(r[7]));
+        else
+          asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
+      }
+    };
+    static_for<KBQ>([&](auto kbc) {
+      constexpr int kb = decltype(kbc)::value;
+      // ---- S^T = K Q^T, dP^T = V dO^T (32 keys x this wave's 32 queries)
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        const int off = kb * 32 * RT::ROW + (r_off ^ (32 * t));
+        const bf16x8 ak = as_bf16x8(*reinterpret_cast<const u32x4 *>(cur + KOFF + off));
+        const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(cur + VOFF + off));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[t], sacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[t], pacc, 0, 0, 0);
+      }
+      // ---- dS^T = P^T o (dP^T - D); element i is key k0 + kb*32 + 8*(i/4) + 4*hf + (i%4)
+      bf16x8 sb[2];
+      auto ds_t = [&](auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           float sv[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int i = 8 * u + j;
-            float x = __builtin_fmaf(sacc[kb][i], c, -lse2);
+            float x = __builtin_fmaf(sacc[i], c, -lse2);
             if (MASK) {
               const int kc = kb * 32 + 8 * (i >> 2) + (i & 3);
               x = (kc <= hi_r && kc >= lo_r) ? x : -INFINITY;    // masked pairs: exp2(-inf) = 0
             }
             const float pr = __builtin_amdgcn_exp2f(x);
-            sv[j] = pr * (pacc[kb][i] - dlt);
+            sv[j] = pr * (pacc[i] - dlt);
           }
           u32x4 sk;
           sk.x = pack_bf16(sv[0], sv[1]);
           sk.y = pack_bf16(sv[2], sv[3]);
           sk.z = pack_bf16(sv[4], sv[5]);
           sk.w = pack_bf16(sv[6], sv[7]);
-          sb[kb][u] = as_bf16x8(sk);
-        }
-    };
-    if (NH == 2 || masked)
-      ds_t(std::true_type{});
-    else
-      ds_t(std::false_type{});
-
-    // ---- dQ^T += K^T dS^T (k = 16 keys per step: kb*32 + 16u + 4hf + (0..3 | 8..11)).
-    //      The transposing reads go through inline asm with explicit waits:
-    //      the compiler cannot tell them apart from the in-flight copies into
-    //      the other stage and would wait for those first.
-    {
-      constexpr int NSTEP = 2 * KBQ, NR = 2 * (D / 32);
-      // one address per 32-column block and read of a pair; the 16-key step
-      // goes into the instructions' immediate offsets
-      const unsigned kbase = static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_void *)(cur + KOFF)));
-      unsigned a_lo[D / 32], a_hi[D / 32];
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        a_lo[db] = kbase + t_off[db];
-        a_hi[db] = kbase + (RT::CPR >= 16 ? (t_off[db] ^ RT::TR8) : t_off[db]) + 8 * RT::ROW;
-      }
-      auto issue = [](auto sc, const unsigned (&lo)[D / 32], const unsigned (&hi)[D / 32], u32x2 (&r)[NR]) {
-        constexpr int off = 16 * decltype(sc)::value * RT::ROW;   // kb * 32 + 16 u rows
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r[2 * db]) : "v"(lo[db]), "n"(off));
-          asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r[2 * db + 1]) : "v"(hi[db]), "n"(off));
+          sb[u] = as_bf16x8(sk);
         }
       };
+      // FULL, complete tiles skip the per-pair mask (uniform over the workgroup)
+      if (masked)
+        ds_t(std::true_type{});
+      else
+        ds_t(std::false_type{});
+      // ---- dQ^T += K^T dS^T (k = 16 keys per step: kb*32 + 16u + 4hf + (0..3 | 8..11))
       u32x2 rr[2][NR];
-      issue(std::integral_constant<int, 0>{}, a_lo, a_hi, rr[0]);
-      static_for<NSTEP>([&](auto stc) {
-        constexpr int st = decltype(stc)::value;
-        u32x2 (&r)[NR] = rr[st & 1];
-        if constexpr (st + 1 < NSTEP) {
-          issue(std::integral_constant<int, st + 1>{}, a_lo, a_hi, rr[(st + 1) & 1]);
-          if constexpr (NR == 8)
-            asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]),
-                         "+v"(r[5]), "+v"(r[6]), "+v"(r[7]));
-          else
-            asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
-        } else {
-          if constexpr (NR == 8)
-            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]),
-                         "+v"(r[5]), "+v"(r[6]), "+v"(r[7]));
-          else
-            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
-        }
-        constexpr int kb = st >> 1, u = st & 1;
+      issue(std::integral_constant<int, 2 * kb>{}, a_lo, a_hi, rr[0]);
+      issue(std::integral_constant<int, 2 * kb + 1>{}, a_lo, a_hi, rr[1]);
+      static_for<2>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        wait_reads(std::integral_constant<bool, u == 0>{}, rr[u]);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 ak = as_bf16x8(u32x4{r[2 * db].x, r[2 * db].y, r[2 * db + 1].x, r[2 * db + 1].y});
-          qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, sb[kb][u], qacc[db], 0, 0, 0);
+          const bf16x8 ak = as_bf16x8(u32x4{rr[u][2 * db].x, rr[u][2 * db].y, rr[u][2 * db + 1].x, rr[u][2 * db + 1].y});
+          qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, sb[u], qacc[db], 0, 0, 0);
         }
       });
-    }
+    });
 
     // the next half's copies have landed and every wave is done with this stage
     __syncthreads();
