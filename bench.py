@@ -420,6 +420,32 @@ def main():
             "value": round(fwd_flop / (ms_c * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "ms_per_step": round(ms_c, 4),
             "kernels": {"attn_fwd": kernel_stats(tm_c, "attn_fwd", fwd_flop)}}
         rc.close()
+        # two calls: the rank's own chunks, then every remote chunk at once (merged)
+        rr = RankForward.local_then_remote(w.cu, w.q_segs, kv_steps, w.hq, w.hkv, w.d, w.scale)
+
+        def two_calls(tm):
+            tm.run("attn_fwd", lambda: sap.sap_attn_fwd(rr.plans[0], q, k, v, qs, ks, w.hq, w.hkv, w.d, w.scale,
+                                                        rr.o, rr.lse))
+            tm.run("attn_fwd", lambda: sap.sap_attn_fwd_merge(rr.plans[1], q, k, v, qs, ks, w.hq, w.hkv, w.d,
+                                                              w.scale, rr.o, rr.lse))
+        warm = _Timer(stream)
+        for _ in range(a.warmup):
+            two_calls(warm)
+        torch.cuda.synchronize()
+        tm_r = _Timer(stream)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(a.steps):
+            two_calls(tm_r)
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms_r = start.elapsed_time(end) / a.steps
+        line["forward_local_then_remote"] = {
+            "step": "forward as two calls: the rank's own chunks, then all remote chunks at once (merge in the "
+                    "epilogue)",
+            "value": round(fwd_flop / (ms_r * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "ms_per_step": round(ms_r, 4),
+            "kernels": {"attn_fwd": kernel_stats(tm_r, "attn_fwd", fwd_flop)}}
+        rr.close()
         # reference: the same forward with a separate merge pass per step
         tm_2, ms_2 = timed(False, fused=False)
         _, value_2, kernels_2 = report(tm_2, ms_2, False)

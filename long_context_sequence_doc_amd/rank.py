@@ -122,6 +122,16 @@ class RankForward:
         self.plans = []
 
     @classmethod
+    def local_then_remote(cls, cu_seqlens, q_segs, step_kv_segs, hq: int, hkv: int, d: int, scale: float,
+                          device: str = "cuda", block_m: int = 0):
+        """Two calls: the rank's own chunks (step 0), then one merged call over
+        the KV of every later step together -- the schedule of a rank that
+        fetches all the remote chunks its plan needs at once (from their
+        owners, in parallel) while it computes on its own chunks."""
+        remote = [seg for segs in step_kv_segs[1:] for seg in segs]
+        return cls(cu_seqlens, q_segs, [step_kv_segs[0], remote], hq, hkv, d, scale, device, block_m=block_m)
+
+    @classmethod
     def concatenated(cls, cu_seqlens, q_segs, step_kv_segs, hq: int, hkv: int, d: int, scale: float,
                      device: str = "cuda", block_m: int = 0):
         """One forward call over every step's KV segments together (the steps

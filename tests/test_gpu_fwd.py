@@ -292,6 +292,29 @@ def test_balanced_rank_sampled():
     rf.close()
 
 
+def test_zigzag_local_then_remote_sampled():
+    """128K zigzag GQA rank 3 as two calls: its own chunks, then every remote
+    chunk together with the merge in the epilogue; sampled rows."""
+    _sap()
+    import torch
+    from long_context_sequence_doc_amd.rank import RankForward
+    w = W.zigzag_rank(3)
+    t = tensors("zigzag")
+    say("case zigzag_sp8_128k_gqa_rank3: local step + one merged call over all remote chunks, sampled rows")
+    rf = RankForward.local_then_remote(w.cu, w.q_segs, [s.kv_segs for s in w.steps], w.hq, w.hkv, w.d, w.scale)
+    assert rf.active == [0, 1]
+    q = to_dev(W.local_rows(t.q, w.q_segs))
+    k, v = to_dev(t.k), to_dev(t.v)
+    rf.run(q, k, v, q.stride(0), k.stride(0))
+    torch.cuda.synchronize()
+    gq = w.q_global_rows()
+    rows = sample_rows(gq, w.cu)
+    ro, rl = A.forward(f64(W.local_rows(t.q, w.q_segs)), f64(t.k), f64(t.v), gq, np.arange(w.total), w.cu, w.scale,
+                       rows=rows)
+    compare(rf.o.cpu().numpy(), rf.lse.cpu().numpy(), ro, rl, rows=rows, label="zigzag local + remote")
+    rf.close()
+
+
 def test_training_forward_sampled():
     _sap()
     say("case train_64k_5heads forward, sampled rows")
