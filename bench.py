@@ -483,6 +483,38 @@ def main():
                         "attn_bwd": kernel_stats(tm_c, "attn_bwd", bwd_flop)}}
         rc.close()
         rbc.close()
+        # the same training step as two calls each: own chunks, then all remote chunks at once
+        rr = RankForward.local_then_remote(w.cu, w.q_segs, kv_steps, w.hq, w.hkv, w.d, w.scale)
+        rbr = RankBackward.local_then_remote(w.cu, w.q_segs, kv_steps, w.hq, w.hkv, w.d, w.scale)
+
+        def two_train(tm):
+            tm.run("attn_fwd", lambda: sap.sap_attn_fwd(rr.plans[0], q, k, v, qs, ks, w.hq, w.hkv, w.d, w.scale,
+                                                        rr.o, rr.lse))
+            tm.run("attn_fwd", lambda: sap.sap_attn_fwd_merge(rr.plans[1], q, k, v, qs, ks, w.hq, w.hkv, w.d,
+                                                              w.scale, rr.o, rr.lse))
+            tm.run("bwd_rowterm", lambda: rbr.rowterm(rr.o, dout, qs))
+            for i in rbr.active:
+                tm.run("attn_bwd", lambda: rbr.accumulate(i, q, k, v, rr.lse, dout, qs, ks, dq, dk, dv))
+        warm = _Timer(stream)
+        for _ in range(a.warmup):
+            two_train(warm)
+        torch.cuda.synchronize()
+        tm_c = _Timer(stream)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(a.steps):
+            two_train(tm_c)
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms_c = start.elapsed_time(end) / a.steps
+        line["training_step_local_then_remote"] = {
+            "step": "forward + backward as two calls each: the rank's own chunks, then all remote chunks at once",
+            "value": round((fwd_flop + bwd_flop) / (ms_c * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+            "ms_per_step": round(ms_c, 4),
+            "kernels": {"attn_fwd": kernel_stats(tm_c, "attn_fwd", fwd_flop),
+                        "attn_bwd": kernel_stats(tm_c, "attn_bwd", bwd_flop)}}
+        rr.close()
+        rbr.close()
     if with_bwd and not headline_bwd:
         # the same shard's training step: forward + recompute backward
         tm_t, ms_t = timed(True)

@@ -199,6 +199,14 @@ class RankBackward:
         self.plans = []
 
     @classmethod
+    def local_then_remote(cls, cu_seqlens, q_segs, step_kv_segs, hq: int, hkv: int, d: int, scale: float,
+                          device: str = "cuda"):
+        """Two accumulate calls: the rank's own chunks, then every later step's
+        KV together (the backward of RankForward.local_then_remote)."""
+        remote = [seg for segs in step_kv_segs[1:] for seg in segs]
+        return cls(cu_seqlens, q_segs, [step_kv_segs[0], remote], hq, hkv, d, scale, device)
+
+    @classmethod
     def concatenated(cls, cu_seqlens, q_segs, step_kv_segs, hq: int, hkv: int, d: int, scale: float,
                      device: str = "cuda"):
         """The backward of every step's KV segments as one call (the steps must

@@ -199,7 +199,7 @@ def test_training_fwd_bwd_sampled():
     rf.close()
 
 
-def _rank_fwd_bwd_sampled(w, label, active=None):
+def _rank_fwd_bwd_sampled(w, label, active=None, two_calls=False):
     """Forward over the ring steps with merges, row terms once, backward per
     non-empty step; sampled dQ rows and dK/dV rows of KV head 0 against the
     oracle's own forward/backward."""
@@ -207,8 +207,12 @@ def _rank_fwd_bwd_sampled(w, label, active=None):
     from long_context_sequence_doc_amd.rank import RankBackward, RankForward
     t = tensors("zigzag", True)
     steps = [s.kv_segs for s in w.steps]
-    rf = RankForward(w.cu, w.q_segs, steps, w.hq, w.hkv, w.d, w.scale)
-    rb = RankBackward(w.cu, w.q_segs, steps, w.hq, w.hkv, w.d, w.scale)
+    if two_calls:
+        rf = RankForward.local_then_remote(w.cu, w.q_segs, steps, w.hq, w.hkv, w.d, w.scale)
+        rb = RankBackward.local_then_remote(w.cu, w.q_segs, steps, w.hq, w.hkv, w.d, w.scale)
+    else:
+        rf = RankForward(w.cu, w.q_segs, steps, w.hq, w.hkv, w.d, w.scale)
+        rb = RankBackward(w.cu, w.q_segs, steps, w.hq, w.hkv, w.d, w.scale)
     if active is not None:
         assert rb.active == active
     ql, dol = W.local_rows(t.q, w.q_segs), W.local_rows(t.do, w.q_segs)
@@ -241,7 +245,7 @@ def _rank_fwd_bwd_sampled(w, label, active=None):
     #     non-empty step's chunks: the oracle forward on all rows of those heads
     grp = w.hq // w.hkv
     cols = set()
-    for st in [w.steps[i] for i in rb.active]:
+    for st in [w.steps[i] for i in range(len(w.steps)) if two_calls or i in rb.active]:
         for a_, b_, _ in st.kv_segs:
             cols.update(rng.integers(a_, b_, size=6).tolist())
             cols.update((a_, b_ - 1))
@@ -264,6 +268,14 @@ def test_zigzag_rank_fwd_bwd_sampled():
     _sap()
     say("case zigzag_sp8_128k_gqa_rank3 fwd+bwd (ring steps), sampled rows")
     _rank_fwd_bwd_sampled(W.zigzag_rank(3), "zigzag", active=[0, 1, 7])
+
+
+def test_zigzag_rank_two_calls_sampled():
+    """128K zigzag GQA rank 3, forward and backward as two calls each (own
+    chunks, then all remote chunks at once)."""
+    _sap()
+    say("case zigzag_sp8_128k_gqa_rank3 fwd+bwd as local + remote calls, sampled rows")
+    _rank_fwd_bwd_sampled(W.zigzag_rank(3), "zigzag two calls", active=[0, 1], two_calls=True)
 
 
 def test_balanced_rank_fwd_bwd_sampled():
