@@ -172,7 +172,7 @@ def rank_sweep(w, t, a, stream):
     k, v = dev(t.k), dev(t.v)
     out = {}
     for tag, own, ch in (base, ("balanced", owner.tolist(), BALANCE_CHUNK)):
-        flop, rank_ms, step_ms, fetched, one_ms = [], [], [], [], []
+        flop, rank_ms, step_ms, fetched, touched, one_ms = [], [], [], [], [], []
         for r in range(p):
             wr = W.owner_rank(w, own, r, ch, tag)
             rf = RankForward(wr.cu, wr.q_segs, [s.kv_segs for s in wr.steps], wr.hq, wr.hkv, wr.d, wr.scale)
@@ -196,6 +196,8 @@ def rank_sweep(w, t, a, stream):
             step_ms.append(per_step)
             rank_ms.append(sum(per_step))
             fetched.append(sum(e - b for i in rf.active if i > 0 for b, e, _ in wr.steps[i].kv_segs))
+            # rows of the remote 64-row KV tiles the plans touch (chunks are whole tiles)
+            touched.append(sum(rf.infos[i]["n_touched_kv_tiles"] * 64 for i in rf.active if i > 0))
             rf.close()
             # the same rank as one call over all the KV it needs (no ring steps, no merge)
             rc = RankForward.concatenated(wr.cu, wr.q_segs, [s.kv_segs for s in wr.steps], wr.hq, wr.hkv, wr.d,
@@ -227,12 +229,15 @@ def rank_sweep(w, t, a, stream):
             "lockstep_ring_ms": round(lockstep, 4),
             "lockstep_ring_tflops_per_gpu": round(sum(flop) / (lockstep * 1e-3) / 1e12 / p, 1),
             "remote_kv_rows_fetched": fetched,
+            "remote_kv_rows_touched": touched,
             "single_call_ms": [round(x, 4) for x in one_ms],
             "single_call_job_tflops_per_gpu": round(sum(flop) / (max(one_ms) * 1e-3) / 1e12 / p, 1),
         }
     out["note"] = ("each rank's forward (ring steps, fused merges) timed alone on this one GPU; job_ms = slowest "
                    "rank (KV fetched as needed), lockstep_ring_ms = sum over ring steps of the slowest rank's step, "
-                   "single_call_ms = the rank as one call over all the KV it needs; communication not included")
+                   "single_call_ms = the rank as one call over all the KV it needs; remote_kv_rows_fetched counts whole "
+                   "remote chunks of non-empty steps, remote_kv_rows_touched only the 64-row KV tiles their plans "
+                   "touch; communication not included")
     return out
 
 
