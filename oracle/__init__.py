@@ -29,8 +29,14 @@ What it computes, and the passage each part follows:
   pair, and whether each is FULL, DIAGONAL or PARTIAL. This is the one-device
   analogue of the HSAP summary page's method section: schedules are generated
   ahead of time for incomplete tensors and irregular attention.
+* ``balance.balance``        -- which rank holds each chunk of query rows, so
+  that ranks with equal token counts get nearly equal attention work. HSAP
+  summary page, technical contributions (load balance across devices by
+  scheduling); SP blog page, future trends and challenges (uneven lengths
+  leave GPUs idle). The rule itself is a reading: heaviest chunk first to the
+  least-loaded rank with room.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against brute force,
-closed forms, a library routine (torch's scaled_dot_product_attention in
+closed forms, hand-worked examples, a library routine (torch's scaled_dot_product_attention in
 float64 on each document alone, torch.autograd) and invariants.
 """
