@@ -108,6 +108,43 @@ def test_random_small_layouts(seed):
     assert (dq.cpu().numpy()[~vq] == 0).all() and (dk.cpu().numpy()[~vk] == 0).all()
 
 
+@pytest.mark.parametrize("case", [(2, 1, 128, [4096]), (1, 1, 64, [3000, 1096]), (4, 2, 128, [1500, 2596])])
+def test_split_kv_tiles_all_rows(case):
+    """Documents long enough that KV tiles meet more partner Q tiles than one
+    workgroup takes: their chunks leave partial sums in workspace slots and
+    the ordered reduce adds them. Every dQ, dK, dV row against the oracle."""
+    sap = _sap()
+    import torch
+    hq, hkv, d, lengths = case
+    cu = W.cu_seqlens(lengths)
+    total = int(cu[-1])
+    scale = 1.0 / np.sqrt(d)
+    say(f"case bwd split tiles hq={hq} hkv={hkv} d={d} docs={lengths}")
+    rs = np.random.default_rng(40 + hq + d)
+    mk = lambda h: W.bf16_round(rs.standard_normal((total, h, d), dtype=np.float32))
+    qb, kb, vb, dob = mk(hq), mk(hkv), mk(hkv), mk(hq)
+    g = np.arange(total)
+    o_ref, lse_ref = A.forward(f64(qb), f64(kb), f64(vb), g, g, cu, scale)
+    dq_ref, dk_ref, dv_ref = A.backward(f64(qb), f64(kb), f64(vb), f64(dob), o_ref, lse_ref, g, g, cu, scale)
+    segs = [(0, total, 0)]
+    plan = sap.sap_plan(cu, segs, segs, 64, 128)
+    # the plan must split some KV tile: workspace beyond the row terms
+    assert sap.sap_attn_bwd_workspace(plan, hq, hkv, d) > hq * total * 4 + 256
+    sap.sap_plan_free(plan)
+    qd, kd, vd, dod = to_dev(qb), to_dev(kb), to_dev(vb), to_dev(dob)
+    o = torch.from_numpy(o_ref.astype(np.float32)).cuda()
+    lse = torch.from_numpy(lse_ref.astype(np.float32)).cuda()
+    dq = torch.zeros((total, hq, d), device="cuda")
+    dk = torch.zeros((total, hkv, d), device="cuda")
+    dv = torch.zeros((total, hkv, d), device="cuda")
+    keep = _bwd_call(sap, cu, segs, segs, qd, kd, vd, dod, o, lse, hq, hkv, d, scale, dq, dk, dv)
+    torch.cuda.synchronize()
+    del keep
+    _check("dQ split", dq.cpu().numpy(), dq_ref)
+    _check("dK split", dk.cpu().numpy(), dk_ref)
+    _check("dV split", dv.cpu().numpy(), dv_ref)
+
+
 def test_ring_steps_accumulate_to_full_gradient():
     """Per-step calls with the final LSE add up (dq/dk/dv are accumulated)."""
     sap = _sap()
