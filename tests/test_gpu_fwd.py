@@ -120,6 +120,38 @@ def test_random_small_layouts(seed, block_m):
     compare(o, lse, ro, rl, rows=rows, label=f"random{seed}/{block_m}")
 
 
+@pytest.mark.parametrize("block_m", [128, 256])
+@pytest.mark.parametrize("hq,hkv,qscale", [(8, 2, 4.0), (3, 3, 4.0), (4, 1, 1.0)])
+def test_long_documents_all_rows(hq, hkv, qscale, block_m):
+    """Documents of thousands of tokens (long partner lists, many online
+    softmax steps) and, with queries scaled by 4 (score spread ~16), frequent
+    moves of the running max past the rescale threshold; every row."""
+    sap = _sap()
+    import torch
+    lengths = [5000, 1, 2191, 1000]
+    cu = W.cu_seqlens(lengths)
+    total = int(cu[-1])
+    d = 128
+    scale = 1.0 / np.sqrt(d)
+    say(f"case long documents {lengths} hq={hq} hkv={hkv} qscale={qscale} block_m={block_m}")
+    rs = np.random.default_rng(77 + hq)
+    qb = W.bf16_round(qscale * rs.standard_normal((total, hq, d), dtype=np.float32))
+    kb = W.bf16_round(rs.standard_normal((total, hkv, d), dtype=np.float32))
+    vb = W.bf16_round(rs.standard_normal((total, hkv, d), dtype=np.float32))
+    segs = [(0, total, 0)]
+    plan = sap.sap_plan(cu, segs, segs, block_m, 64)
+    sap.sap_plan_upload(plan)
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    o = torch.full((total, hq, d), float("nan"), device="cuda")
+    lse = torch.full((hq, total), float("nan"), device="cuda")
+    sap.sap_attn_fwd(plan, q, k, v, q.stride(0), k.stride(0), hq, hkv, d, scale, o, lse)
+    torch.cuda.synchronize()
+    g = np.arange(total)
+    ro, rl = A.forward(f64(qb), f64(kb), f64(vb), g, g, cu, scale)
+    compare(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, label=f"long docs hq={hq} x{qscale} bm={block_m}")
+    sap.sap_plan_free(plan)
+
+
 def test_forward_is_deterministic():
     sap = _sap()
     w = W.ring_rank(3)
