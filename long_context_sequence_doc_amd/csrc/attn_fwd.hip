@@ -24,13 +24,19 @@
 //     A operand is two ds_read_b64_tr_b16 transposing reads of 4 keys each
 //     from row-major V.
 //   * K and V tiles go from global memory straight into LDS
-//     (global_load_lds_dwordx4: no registers, no VALU) into a double buffer:
-//     the next tile's loads are issued before the current tile's math and
-//     waited for at the barrier that ends it. Each load instruction fills
-//     1 KB of LDS, 16 bytes per lane in lane order, so the layout is chosen
-//     through the global address each lane loads: rows are unpadded and the
-//     16-byte chunks of a row are XOR-swizzled by the row index, which keeps
-//     the matrix-operand reads free of bank conflicts.
+//     (global_load_lds_dwordx4: no registers, no VALU) into a double buffer;
+//     copies issued in an iteration are waited for at the barrier that ends
+//     it. Each load instruction fills 1 KB of LDS, 16 bytes per lane in lane
+//     order, so the layout is chosen through the global address each lane
+//     loads: rows are unpadded and the 16-byte chunks of a row are
+//     XOR-swizzled by the row index, which keeps the matrix-operand reads
+//     free of bank conflicts.
+//   * Eight-wave workgroups run a software pipeline with K one tile ahead
+//     of V: while the vector ALUs turn tile j's scores into P_j, the matrix
+//     cores already compute tile j+1's scores (the two waves a SIMD holds
+//     are barrier-locked in the same phase, so without this the matrix
+//     cores idle through the softmax). Four-wave workgroups (several per CU)
+//     keep the plain double buffer.
 //   * Online softmax in fp32 with exp2 and the scale folded into one FMA.
 //     The running max is only moved (and O, l rescaled) when it grows by
 //     more than 2^8, which keeps the result exact (O / l normalises) while
@@ -44,6 +50,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -127,23 +134,20 @@ __device__ inline LoadOffsets<D, NT> load_offsets(int stride, int wave, int lane
   return o;
 }
 
-// Issues the direct global -> LDS copies of one KV tile into a stage.
-template <int D, int NT>
-__device__ inline void issue_tile(const FwdParams &p, const PartnerEntry &pe, int g, unsigned char *stage,
+// Issues the direct global -> LDS copies of one KV tile's K rows (V = false)
+// or V rows (V = true) into a stage.
+template <int D, int NT, bool V>
+__device__ inline void issue_half(const FwdParams &p, const PartnerEntry &pe, int g, unsigned char *stage,
                                   int wave, int lane, const LoadOffsets<D, NT> &full) {
   using G = Stage<D, NT>;
   const int64_t base = int64_t(pe.local_start) * p.kv_row_stride + int64_t(g) * D;
-  const unsigned short *kb = p.k + base;
-  const unsigned short *vb = p.v + base;
+  const unsigned short *src = (V ? p.v : p.k) + base;
   const LoadOffsets<D, NT> o = pe.n == BN ? full : load_offsets<D, NT>(int(p.kv_row_stride), wave, lane, pe.n);
 #pragma unroll
   for (int i = 0; i < G::LOADS; ++i)
-    __builtin_amdgcn_global_load_lds((global_void *)(kb + o.k[i]),
-                                     (lds_void *)(stage + (i * (NT / 64) + wave) * 1024), 16, 0, 0);
-#pragma unroll
-  for (int i = 0; i < G::LOADS; ++i)
-    __builtin_amdgcn_global_load_lds((global_void *)(vb + o.v[i]),
-                                     (lds_void *)(stage + G::TILE + (i * (NT / 64) + wave) * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((global_void *)(src + (V ? o.v[i] : o.k[i])),
+                                     (lds_void *)(stage + (V ? G::TILE : 0) + (i * (NT / 64) + wave) * 1024),
+                                     16, 0, 0);
 }
 
 __device__ inline bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -163,7 +167,7 @@ __device__ inline unsigned pack_bf16(float lo, float hi) {
 // TM: rows of the plan's Q tiles (128 or 256), one 32-row slice per wave;
 // NH: query heads per workgroup (2 only with TM = 128).
 template <int D, bool MERGE, int TM, int NH>
-__global__ __launch_bounds__(2 * TM * NH) void attn_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(2 * TM * NH) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_kernel(FwdParams p) {
   constexpr int WPH = TM / 32;                    // waves per query head
   constexpr int NT = 64 * WPH * NH;
   static_assert(NH == 1 || TM == 128, "two heads per workgroup only with 128-row tiles");
@@ -227,34 +231,26 @@ __global__ __launch_bounds__(2 * TM * NH) void attn_fwd_kernel(FwdParams p) {
       v_off[db] = ST::TILE + vrow * ST::ROW + 16 * ((col >> 3) ^ ST::vsw(vrow)) + 2 * (col & 7);
     }
   }
-  const PartnerEntry *pes = p.partners + rg.begin;
-  PartnerEntry pe = pes[0];
-  issue_tile<D, NT>(p, pe, g, lds, wave, lane, full_offs);
-  __syncthreads();
-
-  for (int it = 0; it < rg.count; ++it) {
-    const unsigned char *cur_stage = lds + (it & 1) * ST::BYTES;
-    const PartnerEntry cur = pe;
-    const bool more = it + 1 < rg.count;
-    if (more) {
-      pe = pes[it + 1];
-      issue_tile<D, NT>(p, pe, g, lds + ((it + 1) & 1) * ST::BYTES, wave, lane, full_offs);
-    }
-
-    // S^T for 64 keys x this wave's 32 queries: two independent accumulator
-    // chains (key blocks) interleaved so each LDS read is issued ahead of use
-    f32x16 s[2] = {f32x16{}, f32x16{}};
-    {
+  // S^T of 64 keys x this wave's 32 queries from the K tile of a stage: two
+  // independent accumulator chains (key blocks)
+  auto scores = [&](f32x16 (&s)[2], const unsigned char *stage) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        const unsigned char *kp = cur_stage + (k_off ^ (32 * t));
-        const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const u32x4 *>(kp));
-        const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + 32 * ST::ROW));
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[t], s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[t], s[1], 0, 0, 0);
-      }
+    for (int t = 0; t < D / 16; ++t) {
+      const unsigned char *kp = stage + (k_off ^ (32 * t));
+      const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const u32x4 *>(kp));
+      const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + 32 * ST::ROW));
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[t], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[t], s[1], 0, 0, 0);
     }
+  };
 
+  // Everything after S^T for one tile: mask by class, online softmax, O^T +=
+  // V^T P^T from the V tile of a stage. `overlap` runs between the max
+  // update and the exponentials; its matrix work (the next tile's scores)
+  // does not depend on them, so the two interleave.
+  auto tile_math = [&](f32x16 (&s)[2], const PartnerEntry &cur, const unsigned char *stage, auto &&overlap) {
     if (cur.cls != SAP_TILE_FULL || cur.n < BN) {
       // allowed keys of this lane's query, as tile-local key indices [lo, hi];
       // element i of key block kb holds key kbase + kb*32 + 8*(i/4) + (i%4)
@@ -289,6 +285,8 @@ __global__ __launch_bounds__(2 * TM * NH) void attn_fwd_kernel(FwdParams p) {
     }
     const float mc = m_used == -INFINITY ? 0.f : m_used * c;
 
+    overlap();
+
     // P = 2^(s c - m c); B operands of O^T += V^T P^T
     bf16x8 pb[2][2];
 #pragma unroll
@@ -297,9 +295,9 @@ __global__ __launch_bounds__(2 * TM * NH) void attn_fwd_kernel(FwdParams p) {
       for (int u = 0; u < 2; ++u) {
         float e[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * u + j], c, -mc));
-          l_part += e[j];
+        for (int q = 0; q < 8; ++q) {
+          e[q] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * u + q], c, -mc));
+          l_part += e[q];
         }
         u32x4 pk;
         pk.x = pack_bf16(e[0], e[1]);
@@ -309,26 +307,111 @@ __global__ __launch_bounds__(2 * TM * NH) void attn_fwd_kernel(FwdParams p) {
         pb[kb][u] = as_bf16x8(pk);
       }
 
-    // O^T += V^T P^T: the D/32 output blocks are independent chains, so the
-    // inner loop over them keeps several MFMAs and LDS reads in flight
-    {
+    // O^T += V^T P^T: the D/32 output blocks are independent chains
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            // keys kb*32 + 16u + 4hf + (0..3 | 8..11): rows +0 and +8 of the lane's 4-row group
-            const unsigned char *vp = cur_stage + v_off[db] + (kb * 32 + 16 * u) * ST::ROW;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vp));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vp + 8 * ST::ROW));
-            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][u], oacc[db], 0, 0, 0);
-          }
-    }
+        for (int db = 0; db < D / 32; ++db) {
+          // keys kb*32 + 16u + 4hf + (0..3 | 8..11): rows +0 and +8 of the lane's 4-row group
+          const unsigned char *vp = stage + v_off[db] + (kb * 32 + 16 * u) * ST::ROW;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vp));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vp + 8 * ST::ROW));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][u], oacc[db], 0, 0, 0);
+        }
+    // keeps the denominator's additions in this tile (otherwise they sink
+    // past the barrier and hold the tile's P values in registers)
+    asm volatile("" : "+v"(l_part));
+  };
 
-    // the next tile's copies have landed and every wave is done with this one
+  // Partner entries are wave-uniform: each is read by a vector load one
+  // iteration before its first use and moved to scalar registers after the
+  // barrier that ends that iteration (whose wait covers the load), so no
+  // wait for it lands inside an iteration.
+  const PartnerEntry *pes = p.partners + rg.begin;
+  const int cnt = __builtin_amdgcn_readfirstlane(rg.count);
+  auto uniform = [](const PartnerEntry &e) {
+    return PartnerEntry{__builtin_amdgcn_readfirstlane(e.local_start), __builtin_amdgcn_readfirstlane(e.global_start),
+                        __builtin_amdgcn_readfirstlane(e.n), __builtin_amdgcn_readfirstlane(e.cls)};
+  };
+  auto raw = [&](int i) { return pes[i < cnt ? i : 0]; };
+  PartnerEntry e0 = uniform(raw(0));
+  PartnerEntry e1 = uniform(raw(1));
+
+  if constexpr (NT >= 512) {
+    // Eight waves: software pipeline over the partner tiles, K one tile
+    // ahead of V. When iteration j starts, S_j is in registers and K_{j+1}
+    // and V_j are in LDS (stages (j+1) % 2 and j % 2). The iteration issues
+    // the copies of K_{j+2} (into K_j's slot) and V_{j+1} (into V_{j-1}'s
+    // slot), turns S_j into P_j on the vector ALUs while the matrix cores
+    // compute S_{j+1}, adds V_j P_j into O, and ends at a barrier that makes
+    // its copies visible and frees the slots it read.
+    PartnerEntry e2 = uniform(raw(2));
+    issue_half<D, NT, false>(p, e0, g, lds, wave, lane, full_offs);
+    issue_half<D, NT, true>(p, e0, g, lds, wave, lane, full_offs);
+    if (cnt > 1) issue_half<D, NT, false>(p, e1, g, lds + ST::BYTES, wave, lane, full_offs);
     __syncthreads();
+    f32x16 sA[2], sB[2];
+    scores(sA, lds);
+    __syncthreads();   // every wave has read K_0 before K_2 replaces it
+
+    auto body = [&](f32x16 (&s)[2], f32x16 (&s_next)[2], int j, auto has_next) {
+      constexpr bool HN = decltype(has_next)::value;
+      unsigned char *stage_j = lds + (j & 1) * ST::BYTES;
+      unsigned char *stage_n = lds + ((j + 1) & 1) * ST::BYTES;
+      if (j + 2 < cnt) issue_half<D, NT, false>(p, e2, g, stage_j, wave, lane, full_offs);
+      if (HN) issue_half<D, NT, true>(p, e1, g, stage_n, wave, lane, full_offs);
+      const PartnerEntry raw3 = raw(j + 3);
+      tile_math(s, e0, stage_j, [&] {
+        if (HN) scores(s_next, stage_n);
+      });
+      // the copies have landed and every wave is done with this iteration's slots
+      __syncthreads();
+      // nothing moves above the barrier: the entry load's wait stays behind it
+      __builtin_amdgcn_sched_barrier(0);
+      e0 = e1;
+      e1 = e2;
+      e2 = uniform(raw3);
+    };
+
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+    int j = 0;
+    for (; j + 2 < cnt; j += 2) {
+      body(sA, sB, j, yes{});
+      body(sB, sA, j + 1, yes{});
+    }
+    if (cnt - j == 2) {
+      body(sA, sB, j, yes{});
+      body(sB, sA, j + 1, no{});
+    } else {
+      body(sA, sB, j, no{});
+    }
+  } else {
+    // Four waves (more workgroups per CU, which overlap one another's
+    // phases): plain double buffer; the next tile's K and V are copied
+    // while this tile is computed.
+    issue_half<D, NT, false>(p, e0, g, lds, wave, lane, full_offs);
+    issue_half<D, NT, true>(p, e0, g, lds, wave, lane, full_offs);
+    __syncthreads();
+    for (int j = 0; j < cnt; ++j) {
+      unsigned char *stage_j = lds + (j & 1) * ST::BYTES;
+      unsigned char *stage_n = lds + ((j + 1) & 1) * ST::BYTES;
+      if (j + 1 < cnt) {
+        issue_half<D, NT, false>(p, e1, g, stage_n, wave, lane, full_offs);
+        issue_half<D, NT, true>(p, e1, g, stage_n, wave, lane, full_offs);
+      }
+      const PartnerEntry raw2 = raw(j + 2);
+      f32x16 s[2];
+      scores(s, stage_j);
+      tile_math(s, e0, stage_j, [] {});
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      e0 = e1;
+      e1 = uniform(raw2);
+    }
   }
 
   // epilogue: O = O / l, LSE = m * scale + ln l
