@@ -17,7 +17,7 @@
 //   * Per 64-key KV tile: S^T = K Q^T with v_mfma_f32_32x32x16_bf16. In the
 //     32x32 accumulator a lane holds one column (= one query) and 16 rows (=
 //     keys), so a query's scores sit in one lane pair (lane, lane ^ 32): row
-//     max/sum are in-register plus a single cross-half exchange.
+//     max/sum are in-register plus one v_permlane32_swap across the halves.
 //   * P^T (bf16) is already in the B-operand layout of O^T += V^T P^T, so P
 //     never goes through LDS. Its registers carry the keys of every 16-key
 //     step in the order (0-3, 8-11 | 4-7, 12-15) (lane halves), so the V^T
@@ -152,6 +152,19 @@ __device__ inline void issue_half(const FwdParams &p, const PartnerEntry &pe, in
 
 __device__ inline bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
+// max / sum of a lane's value and that of lane ^ 32, the same in both lanes.
+// v_permlane32_swap exchanges the upper 32 lanes of its first operand with
+// the lower 32 lanes of its second; with the value passed as both, each
+// lane finds its partner's value in one result and its own in the other.
+__device__ inline float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
@@ -273,7 +286,7 @@ __global__ __launch_bounds__(2 * TM * NH) __attribute__((amdgpu_waves_per_eu(2))
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = xor32_max(mx);
     const bool need = mx > m_used && (m_used == -INFINITY || (mx - m_used) * c > RESCALE_LOG2);
     if (__any(need)) {
       const float m_new = need ? mx : m_used;
@@ -415,7 +428,7 @@ __global__ __launch_bounds__(2 * TM * NH) __attribute__((amdgpu_waves_per_eu(2))
   }
 
   // epilogue: O = O / l, LSE = m * scale + ln l
-  const float l = l_part + __shfl_xor(l_part, 32);
+  const float l = xor32_sum(l_part);
   if (!row_ok) return;
   const int row = wi.local_start + my_row;
   const bool empty = !(l > 0.f);
