@@ -152,6 +152,40 @@ def test_long_documents_all_rows(hq, hkv, qscale, block_m):
     sap.sap_plan_free(plan)
 
 
+@pytest.mark.parametrize("hq,hkv,block_m", [(4, 2, 128), (4, 2, 256), (2, 1, 256), (3, 3, 128)])
+def test_partner_counts_one_to_nineteen(hq, hkv, block_m):
+    """One 1216-token document and Q row ranges chosen so that the Q tiles
+    meet every number of 64-key partner tiles from 1 to 19, odd and even:
+    the eight-wave software pipeline (its two-iteration unrolled loop and
+    both of its tails) and the four-wave loop run every count."""
+    sap = _sap()
+    import torch
+    total, d = 1216, 128
+    cu = [0, total]
+    rs = np.random.default_rng(77)
+    qf = W.bf16_round(rs.standard_normal((total, hq, d), dtype=np.float32))
+    kf = W.bf16_round(rs.standard_normal((total, hkv, d), dtype=np.float32))
+    vf = W.bf16_round(rs.standard_normal((total, hkv, d), dtype=np.float32))
+    counts = set()
+    for a, b in [(0, 64), (0, 128), (0, 192), (0, total), (64, total), (128, total), (192, total)]:
+        say(f"case partner counts hq={hq} hkv={hkv} block_m={block_m} q_rows=[{a},{b})")
+        plan = sap.sap_plan(cu, [(a, b, 0)], [(0, total, 0)], block_m, 64)
+        info = sap.sap_plan_info(plan)
+        qt, _, _ = sap.sap_plan_tiles(plan)
+        counts |= set(np.bincount(qt).tolist())
+        qd, kd, vd = to_dev(qf[a:b]), to_dev(kf), to_dev(vf)
+        o = torch.full((info["tq"], hq, d), float("nan"), device="cuda")
+        lse = torch.full((hq, info["tq"]), float("nan"), device="cuda")
+        sap.sap_plan_upload(plan)
+        sap.sap_attn_fwd(plan, qd, kd, vd, qd.stride(0), kd.stride(0), hq, hkv, d, 1.0 / np.sqrt(d), o, lse)
+        torch.cuda.synchronize()
+        ro, rl = A.forward(f64(qf[a:b]), f64(kf), f64(vf), np.arange(a, b), np.arange(total), np.array(cu),
+                           1.0 / np.sqrt(d))
+        compare(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, label=f"counts/{hq}/{hkv}/{block_m}/{a}")
+        sap.sap_plan_free(plan)
+    assert counts == set(range(1, 20)), sorted(counts)
+
+
 def test_forward_is_deterministic():
     sap = _sap()
     w = W.ring_rank(3)
