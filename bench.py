@@ -401,6 +401,28 @@ def main():
         "kernels": kernels,
     }
     if len(rf.active) > 1 and not headline_bwd:
+        # the headline step's launches one by one: each non-empty ring step's
+        # useful FLOP, time and rate (step 0 writes, later steps merge)
+        def by_step(tm):
+            for n, i in enumerate(rf.active):
+                f = sap.sap_attn_fwd if n == 0 else sap.sap_attn_fwd_merge
+                tm.run(i, lambda: f(rf.plans[i], q, k, v, qs, ks, w.hq, w.hkv, w.d, w.scale, rf.o, rf.lse))
+        warm = _Timer(stream)
+        for _ in range(a.warmup):
+            by_step(warm)
+        torch.cuda.synchronize()
+        tm_s = _Timer(stream)
+        for _ in range(a.steps):
+            by_step(tm_s)
+        torch.cuda.synchronize()
+        line["ring_steps"] = []
+        for i in rf.active:
+            inf = rf.infos[i]
+            f_i = inf["useful_pairs_per_head"] * w.hq * 4 * w.d
+            ms_i = tm_s.ms(i) / a.steps
+            line["ring_steps"].append({"step": i, "touched_q_tiles": inf["n_touched_q_tiles"], "tiles": inf["n_tiles"],
+                                       "useful_flop": f_i, "ms": round(ms_i, 4),
+                                       "tflops": round(f_i / (ms_i * 1e-3) / 1e12, 1)})
         # the same forward as one call over all steps' KV (a rank holding every chunk)
         rc = RankForward.concatenated(w.cu, w.q_segs, kv_steps, w.hq, w.hkv, w.d, w.scale)
         rc_plan = rc.plans[0]
