@@ -331,6 +331,29 @@ def test_zigzag_gqa_headline_sampled():
     rf.close()
 
 
+def test_zigzag_single_call_sampled():
+    """128K zigzag GQA shard (rank 3) as one launch over all non-empty steps'
+    KV (concatenated plan, no merges): sampled rows against the oracle."""
+    _sap()
+    import torch
+    from long_context_sequence_doc_amd.rank import RankForward
+    say("case zigzag_sp8_128k_gqa_rank3: one call over all steps' KV, sampled rows")
+    w = W.by_name("zigzag")
+    t = tensors("zigzag")
+    rc = RankForward.concatenated(w.cu, w.q_segs, [s.kv_segs for s in w.steps], w.hq, w.hkv, w.d, w.scale)
+    assert rc.active == [0]
+    q = to_dev(W.local_rows(t.q, w.q_segs))
+    k, v = to_dev(t.k), to_dev(t.v)
+    rc.run(q, k, v, q.stride(0), k.stride(0))
+    torch.cuda.synchronize()
+    gq = w.q_global_rows()
+    rows = sample_rows(gq, w.cu)
+    ro, rl = A.forward(f64(W.local_rows(t.q, w.q_segs)), f64(t.k), f64(t.v), gq, np.arange(w.total), w.cu, w.scale,
+                       rows=rows)
+    compare(rc.o.cpu().numpy(), rc.lse.cpu().numpy(), ro, rl, rows=rows, label="zigzag single call")
+    rc.close()
+
+
 def test_balanced_rank_sampled():
     """128K sequence, document-aware balanced layout (1024-row chunks from
     sap_balance, equal to the oracle's assignment), rank 3: ring steps with
