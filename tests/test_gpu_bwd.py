@@ -326,3 +326,46 @@ def test_balanced_rank_fwd_bwd_sampled():
     w = W.owner_rank(z, owner.tolist(), 3, 1024, "balanced")
     say(f"case balanced_sp8_128k_gqa_rank3 fwd+bwd ({len(w.q_segs)} Q segments), sampled rows")
     _rank_fwd_bwd_sampled(w, "balanced")
+
+
+def test_plans_without_pairs_launch_nothing():
+    """A call whose KV rows all lie after its queries (one document) has no
+    allowed pair: every entry point returns OK and leaves its outputs
+    bit-identical (poisoned buffers stay as they were), with or without an
+    uploaded plan, and the stream stays usable."""
+    sap = _sap()
+    import torch
+    say("case no allowed pair: Q rows [0, 256), KV rows [256, 512) of one 512-token document")
+    hq, hkv, d, total = 4, 2, 128, 512
+    cu = [0, total]
+    for bm, bn in ((128, 64), (64, 128)):
+        plan = sap.sap_plan(cu, [(0, 256, 0)], [(256, total, 0)], bm, bn)
+        info = sap.sap_plan_info(plan)
+        assert info["n_tiles"] == 0 and info["useful_pairs_per_head"] == 0
+        q = torch.randn((256, hq, d), device="cuda").to(torch.bfloat16)
+        kv = torch.randn((256, hkv, d), device="cuda").to(torch.bfloat16)
+        o = torch.full((256, hq, d), float("nan"), device="cuda")
+        lse = torch.full((hq, 256), 7.0, device="cuda")
+        dq = torch.full((256, hq, d), 3.0, device="cuda")
+        dk = torch.full((256, hkv, d), -2.0, device="cuda")
+        dv = torch.full((256, hkv, d), 5.0, device="cuda")
+        delta = torch.full((hq, 256), 11.0, device="cuda")
+        before = [t.clone() for t in (o, lse, dq, dk, dv, delta)]
+        if bm == 128:
+            sap.sap_attn_fwd(plan, q, kv, kv, q.stride(0), kv.stride(0), hq, hkv, d, 0.088, o, lse)
+            sap.sap_attn_fwd_merge(plan, q, kv, kv, q.stride(0), kv.stride(0), hq, hkv, d, 0.088, o, lse)
+            sap.sap_lse_merge(plan, o, lse, o, lse, 256, hq, d)
+        else:
+            # the row terms still take hq x tq floats; no KV tile, so no partial-sum slots
+            assert sap.sap_attn_bwd_workspace(plan, hq, hkv, d) == hq * 256 * 4
+            assert sap.sap_attn_bwd_workspace(plan, 0, hkv, d) == 0
+            sap.sap_attn_bwd_rowterm(plan, o, q, q.stride(0), hq, d, delta)
+            sap.sap_attn_bwd_accumulate(plan, q, kv, kv, lse, delta, q, q.stride(0), kv.stride(0), hq, hkv, d,
+                                        0.088, dq, dk, dv)
+        torch.cuda.synchronize()
+        for a, b in zip((o, lse, dq, dk, dv, delta), before):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+        sap.sap_plan_free(plan)
+    # the stream still runs work afterwards
+    x = torch.ones(1024, device="cuda")
+    assert float((x * 2).sum()) == 2048.0
