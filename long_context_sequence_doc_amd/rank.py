@@ -45,13 +45,14 @@ N_CU = 256
 def forward_block_m(q_segs, hq: int, hkv: int) -> int:
     """Q tile height of the forward plans: 256 when the GQA group is odd (a
     workgroup then holds one head, and 256-row tiles let 8 waves share each
-    staged K / V tile instead of 4) and the rank has rows enough for about
-    eight such workgroups per compute unit (with fewer, the heaviest tiles
-    leave a tail: the 64K, 5-head shard is 2.5 % slower with 256 rows, the
-    512K, 4-head one 6 % faster); else 128 (even groups pair two heads per
-    workgroup instead)."""
+    staged K / V tile, in the software-pipelined loop, instead of 4 in the
+    plain one) and the rank has rows enough for about four such workgroups
+    per compute unit (the 64K, 5-head shard is 4 % faster with 256 rows, the
+    512K, 4-head one 6 %; the 32K, 32-head ring rank, with two per compute
+    unit, 5 % slower); else 128 (even groups pair two heads per workgroup
+    instead)."""
     tq = max(ls + ge - gs for gs, ge, ls in q_segs)
-    if (hq // hkv) % 2 == 1 and (tq // 256) * hq >= 8 * N_CU:
+    if (hq // hkv) % 2 == 1 and (tq // 256) * hq >= 4 * N_CU:
         return 256
     return BLOCK_M
 
