@@ -9,11 +9,11 @@
 // A side whose LSE is -inf holds no keys and contributes nothing.
 //
 // HBM-bound elementwise work: (12 D + 12) bytes per (row, head). A touched Q
-// tile's rows are one contiguous [rows][Hq][D] block of O, so the blocks of
-// grid row x stream float4s of touched tile x; the (row, head) LSE pair is
-// read by the D/4 threads of its row segment, which all sit in one wave (D is
-// a power of two <= 256), and written back by the first of them after every
-// lane of the wave has read it.
+// tile's rows are one contiguous [rows][Hq][D] block of O; D/4 consecutive
+// threads take one (row, head), one float4 each, so a block pass streams
+// NTHREADS * 16 bytes of each operand. The (row, head) LSE pair is read by
+// those D/4 threads, which sit in one wave (D/4 divides 64), and written
+// back by the first of them after every lane of the wave has read it.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -26,17 +26,20 @@ namespace {
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int NTHREADS = 256;
-constexpr int PER_THREAD = 4;
 
 struct MergeParams {
   float *o_acc, *lse_acc;
   const float *o_part, *lse_part;
   const int32_t *touched_rows;
-  int32_t tq, hq, d, d4;
+  int32_t tq, hq;
   int32_t single_rows;   // rows when merging everything (touched_rows == nullptr)
 };
 
+template <int D>
 __global__ __launch_bounds__(NTHREADS) void lse_merge_kernel(MergeParams p) {
+  constexpr int D4 = D / 4;                      // float4s per (row, head)
+  constexpr int RH = NTHREADS / D4;              // (row, head) pairs per block pass
+  static_assert(64 % D4 == 0, "a (row, head) must sit inside one wave");
   int r0, n;
   if (p.touched_rows) {
     r0 = p.touched_rows[2 * blockIdx.x];
@@ -45,16 +48,13 @@ __global__ __launch_bounds__(NTHREADS) void lse_merge_kernel(MergeParams p) {
     r0 = 0;
     n = p.single_rows;
   }
-  const int64_t per_row4 = int64_t(p.hq) * p.d4;
-  const int64_t total4 = int64_t(n) * per_row4;
-  const int64_t base4 = int64_t(r0) * per_row4;
-  f32x4 *oa = reinterpret_cast<f32x4 *>(p.o_acc) + base4;
-  const f32x4 *ob = reinterpret_cast<const f32x4 *>(p.o_part) + base4;
-  const int64_t stride = int64_t(gridDim.y) * NTHREADS;
-  for (int64_t e = int64_t(blockIdx.y) * NTHREADS + threadIdx.x; e < total4; e += stride) {
-    const int64_t rh = e / p.d4;                 // (row, head) index inside the block
-    const int row = r0 + int(rh / p.hq);
-    const int head = int(rh % p.hq);
+  const int nrh = n * p.hq;                      // (row, head) pairs of this tile (< 2^31, checked on the host)
+  const int c = int(threadIdx.x) % D4;
+  f32x4 *oa = reinterpret_cast<f32x4 *>(p.o_acc) + int64_t(r0) * p.hq * D4;
+  const f32x4 *ob = reinterpret_cast<const f32x4 *>(p.o_part) + int64_t(r0) * p.hq * D4;
+  for (int rh = int(blockIdx.y) * RH + int(threadIdx.x) / D4; rh < nrh; rh += int(gridDim.y) * RH) {
+    const int rr = rh / p.hq;
+    const int row = r0 + rr, head = rh - rr * p.hq;
     const int64_t li = int64_t(head) * p.tq + row;
     const float la = p.lse_acc[li], lb = p.lse_part[li];
     const float mx = fmaxf(la, lb), mn = fminf(la, lb);
@@ -68,9 +68,10 @@ __global__ __launch_bounds__(NTHREADS) void lse_merge_kernel(MergeParams p) {
       wa = la == -INFINITY ? 0.f : __expf(la - L);
       wb = lb == -INFINITY ? 0.f : __expf(lb - L);
     }
+    const int64_t e = int64_t(rh) * D4 + c;
     const f32x4 a = oa[e], b = ob[e];
     oa[e] = wa * a + wb * b;
-    if (e % p.d4 == 0) p.lse_acc[li] = L;
+    if (c == 0) p.lse_acc[li] = L;
   }
 }
 
@@ -85,15 +86,24 @@ hipError_t launch_lse_merge(const MergeLaunch &a, hipStream_t stream) {
   p.touched_rows = a.touched_rows;
   p.tq = a.tq;
   p.hq = a.hq;
-  p.d = a.d;
-  p.d4 = a.d / 4;
   p.single_rows = a.touched_rows ? 0 : a.tq;
-  const int64_t total4 = int64_t(a.max_rows) * a.hq * p.d4;
-  int64_t by = (total4 + int64_t(NTHREADS) * PER_THREAD - 1) / (int64_t(NTHREADS) * PER_THREAD);
+  const int64_t pairs = int64_t(a.max_rows) * a.hq;
+  if (pairs > INT32_MAX / 2) return hipErrorInvalidValue;
+  const int rh = a.d >= 4 && a.d <= 256 ? NTHREADS / (a.d / 4) : 1;
+  int64_t by = (pairs + rh - 1) / rh;
   if (by < 1) by = 1;
   if (by > 65535) by = 65535;
   const dim3 grid{static_cast<unsigned>(a.n_touched), static_cast<unsigned>(by)}, block{NTHREADS};
-  hipLaunchKernelGGL(lse_merge_kernel, grid, block, 0, stream, p);
+  switch (a.d) {   // the head dims the entry point accepts: powers of two in [4, 256]
+    case 4: hipLaunchKernelGGL(lse_merge_kernel<4>, grid, block, 0, stream, p); break;
+    case 8: hipLaunchKernelGGL(lse_merge_kernel<8>, grid, block, 0, stream, p); break;
+    case 16: hipLaunchKernelGGL(lse_merge_kernel<16>, grid, block, 0, stream, p); break;
+    case 32: hipLaunchKernelGGL(lse_merge_kernel<32>, grid, block, 0, stream, p); break;
+    case 64: hipLaunchKernelGGL(lse_merge_kernel<64>, grid, block, 0, stream, p); break;
+    case 128: hipLaunchKernelGGL(lse_merge_kernel<128>, grid, block, 0, stream, p); break;
+    case 256: hipLaunchKernelGGL(lse_merge_kernel<256>, grid, block, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -436,12 +436,14 @@ def test_ulysses_sampled(name):
     rf.close()
 
 
-def test_merge_against_oracle():
-    """sap_lse_merge alone: dense (plan NULL) and plan-restricted, with -inf rows."""
+@pytest.mark.parametrize("d", [4, 32, 64, 128, 256])
+def test_merge_against_oracle(d):
+    """sap_lse_merge alone, every head dim it accepts: dense (plan NULL) and
+    plan-restricted, with -inf rows."""
     sap = _sap()
     import torch
     rng = np.random.default_rng(3)
-    tq, hq, d = 300, 3, 64
+    tq, hq = 300, 3
     oa = rng.standard_normal((tq, hq, d)).astype(np.float32)
     ob = rng.standard_normal((tq, hq, d)).astype(np.float32)
     la = (3 * rng.standard_normal((hq, tq))).astype(np.float32)
@@ -454,7 +456,7 @@ def test_merge_against_oracle():
     lb[2, 20:25] = -np.inf
     oa[20:25, 2] = 0
     ob[20:25, 2] = 0
-    say("case merge dense 300x3x64")
+    say(f"case merge dense 300x3x{d}")
     t = lambda x: torch.from_numpy(x).cuda()
     da, dla = t(oa), t(la)
     sap.sap_lse_merge(None, da, dla, t(ob), t(lb), tq, hq, d)
