@@ -562,9 +562,9 @@ __global__ __launch_bounds__(NT) void bwd_kv_reduce_kernel(const ReduceItem *ite
 constexpr int HK = 64;      // keys per half of a KV tile in the dQ kernel
 
 // dQ kernel: one workgroup = one 64-row Q tile x NH query heads of one KV
-// head (NH = 2 when the GQA group has an even size, so four waves share each
-// staged K / V part-tile). Wave w owns head hq0 + w / 2, rows 32 (w % 2) ..
-// +31. Per part of a partner KV tile (64 keys with two heads; 32 with one,
+// head (NH = 4 when the GQA group size is a multiple of 4, else 2 when it is
+// even, so 8 or 4 waves share each staged K / V part-tile). Wave w owns head hq0 + w / 2, rows 32 (w % 2) ..
+// +31. Per part of a partner KV tile (64 keys with two or four heads; 32 with one,
 // so four 2-wave workgroups fit a CU), staged by direct copies into a
 // double-buffered LDS stage (K rows, V rows; swizzled as RowTile):
 //   S^T = K Q^T, dP^T = V dO^T            (A: K / V rows, B: Q / dO in registers)
@@ -577,7 +577,7 @@ __global__ __launch_bounds__(128 * NH) void attn_bwd_dq_kernel(BwdParams p) {
   constexpr int NWV = 2 * NH;                        // waves
   // keys per stage: 64 (half a KV tile) with two heads per workgroup; 32 (a
   // quarter) with one, so that four 2-wave workgroups fit a CU's LDS
-  constexpr int HKQ = NH == 2 ? HK : HK / 2;
+  constexpr int HKQ = NH >= 2 ? HK : HK / 2;
   constexpr int KBQ = HKQ / 32;                      // 32-key blocks per stage
   constexpr int KOFF = 0, VOFF = HKQ * RT::ROW;      // K, V part-tiles (RowTile rows)
   constexpr int STAGE = 2 * HKQ * RT::ROW;
@@ -874,18 +874,22 @@ hipError_t launch_attn_bwd(const BwdLaunch &a, hipStream_t stream) {
     p.range = a.q_range;
     p.partners = a.q_partners;
     p.n_work = a.n_q_work;
-    const int nh = p.group % 2 == 0 ? 2 : 1;      // query heads per workgroup
+    const int nh = p.group % 4 == 0 ? 4 : p.group % 2 == 0 ? 2 : 1;   // query heads per workgroup
     const int64_t slots = (int64_t(a.n_q_work) * a.hkv + NXCD - 1) / NXCD;
     const int64_t blocks = slots * NXCD * (p.group / nh);
     if (blocks > INT32_MAX) return hipErrorInvalidValue;
     const dim3 grid{static_cast<unsigned>(blocks)};
     if (a.d == 128) {
-      if (nh == 2)
+      if (nh == 4)
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 4>), grid, dim3(512), 0, stream, p);
+      else if (nh == 2)
         hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 2>), grid, dim3(256), 0, stream, p);
       else
         hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 1>), grid, dim3(128), 0, stream, p);
     } else {
-      if (nh == 2)
+      if (nh == 4)
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 4>), grid, dim3(512), 0, stream, p);
+      else if (nh == 2)
         hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 2>), grid, dim3(256), 0, stream, p);
       else
         hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 1>), grid, dim3(128), 0, stream, p);
