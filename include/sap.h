@@ -55,7 +55,7 @@ extern "C" {
 typedef enum {
   SAP_OK = 0,
   SAP_ERR_INVALID_ARG = 1,  /* bad pointer, size, segment table, stride ... */
-  SAP_ERR_UNSUPPORTED = 2,  /* valid but not compiled: head_dim, tile shape */
+  SAP_ERR_UNSUPPORTED = 2,  /* valid but not compiled (head_dim, tile shape) or too large for one dispatch */
   SAP_ERR_NO_MEMORY = 3,    /* host or device allocation failed */
   SAP_ERR_HIP = 4,          /* a HIP runtime call or launch failed */
   SAP_ERR_STATE = 5         /* e.g. a compute call on a plan not uploaded */
@@ -198,9 +198,14 @@ sap_status sap_attn_fwd_merge(sap_plan_t plan, const void *q, const void *k, con
                               float *o_acc, float *lse_acc, void *hip_stream);
 
 /*
- * sap_lse_merge -- exact merge of a partial result into a running one:
+ * sap_lse_merge -- exact merge of a partial result into a running one
+ * (SP blog page, bmjup.com/post/14448.html, FAQ Q1: sequence parallelism is
+ * computation-equivalent to one device, so the ring's partial results must
+ * combine into exactly the full-sequence attention; the log-sum-exp merge is
+ * that combination):
  *   L = ln(e^La + e^Lb);  O = e^(La-L) O_a + e^(Lb-L) O_b
- * (a side with L = -inf contributes nothing; both -inf leaves O = 0,
+ * (a side with L = -inf contributes nothing -- its O is not read into the
+ * result, so it may hold anything, even NaN; both -inf leaves O = 0,
  * L = -inf). In place on o_acc / lse_acc. With a plan, only the rows of its
  * touched Q tiles are read and written -- the rest are unchanged, which is
  * exact since the partial holds no keys for them; with plan == NULL all tq
@@ -212,6 +217,16 @@ sap_status sap_lse_merge(sap_plan_t plan, float *o_acc, float *lse_acc,
                          int32_t tq, int32_t hq, int32_t d, void *hip_stream);
 
 /*
+ * The backward (recompute form). Only O and LSE are kept from the forward;
+ * the probabilities are recomputed from them instead of being stored -- the
+ * attention-level echo of the AutoSP page (gist.science/zh/paper/2604.27089)
+ * section 2.B, which keeps attention's saved state and recomputes the large
+ * intermediates. The gradients are those of the mask and forward above
+ * (HSAP summary page, gptget.net/papers/2606.30460, original abstract; AutoSP
+ * page section 2.A step 4: masks on global positions), and the per-step
+ * calls of a ring add up to the full-sequence gradient (SP blog page,
+ * bmjup.com/post/14448.html, FAQ Q1: computation-equivalent to one device).
+ *
  * sap_attn_bwd_workspace -- device workspace bytes of the backward calls:
  * fp32 row terms D_r = dO_r . O_r ([hq][Tq], omitted when hq == 0) followed
  * by the fp32 partial dK / dV sums of the plan's split KV tiles (the planner
@@ -224,7 +239,8 @@ sap_status sap_lse_merge(sap_plan_t plan, float *o_acc, float *lse_acc,
 size_t sap_attn_bwd_workspace(sap_plan_t plan, int32_t hq, int32_t hkv, int32_t d);
 
 /*
- * sap_attn_bwd -- recompute-based backward of this call's share:
+ * sap_attn_bwd -- recompute-based backward of this call's share (AutoSP page,
+ * gist.science/zh/paper/2604.27089, section 2.B: recompute rather than store):
  *   P = exp(scale q k^T - LSE_final) on allowed pairs, D_r = dO_r . O_final_r,
  *   dV += P^T dO;  dS = P o (dO v^T - D);  dQ += scale dS k;  dK += scale dS^T q.
  * o / lse_final are the merged forward results over *all* KV rows, so the
@@ -232,10 +248,17 @@ size_t sap_attn_bwd_workspace(sap_plan_t plan, int32_t hq, int32_t hkv, int32_t 
  * (+=, fp32); the caller zeroes them once. No atomics: dK/dV come from a
  * KV-major pass and dQ from a Q-major pass, each owning its output rows (a
  * split KV tile's chunks write workspace slots that one pass adds in a fixed
- * order), so the result is deterministic. workspace: device, 16-byte
- * aligned, >= sap_attn_bwd_workspace(plan, hq, hkv, d) bytes; its contents
- * on entry do not matter. Calls sharing one workspace must not overlap.
- * Plan tile shape must be 64 x 128 (block_m x block_n).
+ * order), so the result is deterministic: the same inputs give the same
+ * bits. workspace: device, 16-byte aligned, >= sap_attn_bwd_workspace(plan,
+ * hq, hkv, d) bytes; its contents on entry do not matter. Calls sharing one
+ * workspace must not overlap. q, k, v, dout bf16 and o fp32 as in the
+ * conventions above; lse_final fp32 [Hq][Tq]; hq % hkv == 0, d in {64, 128};
+ * scale > 0 and finite. Plan tile shape must be 64 x 128 (block_m x block_n).
+ * Every argument of both passes (row terms, then dK/dV and dQ) is checked
+ * before anything is launched. Errors: SAP_ERR_INVALID_ARG (NULL or
+ * misaligned pointer, bad stride, workspace too small), SAP_ERR_UNSUPPORTED
+ * (head dim, tile shape, or a plan too large for one dispatch's grid),
+ * SAP_ERR_STATE (plan not uploaded to this device), SAP_ERR_HIP (launch).
  */
 sap_status sap_attn_bwd(sap_plan_t plan, const void *q, const void *k, const void *v,
                         const float *o, const float *lse_final, const void *dout,
@@ -248,21 +271,34 @@ sap_status sap_attn_bwd(sap_plan_t plan, const void *q, const void *k, const voi
  * sap_attn_bwd_rowterm -- the backward's row terms D_r = dO_r . O_r (O the
  * final merged forward output) for the rows of the plan's touched Q tiles,
  * into delta fp32 [Hq][Tq] (device; other rows untouched). HBM-bound.
- * A ring rank computes them once with the plan of its own chunk (which
- * touches every local row) and reuses them for every step's
- * sap_attn_bwd_accumulate. Plan tile shape 64 x 128.
+ * Part of the recompute backward (AutoSP page, gist.science/zh/paper/2604.27089,
+ * section 2.B): D_r replaces the stored probabilities' row sums of P dP.
+ * Because it uses the final O, a ring rank computes it once, with the plan of
+ * its own chunk (which touches every local row), and reuses it for every
+ * step's sap_attn_bwd_accumulate -- so the steps add up to the one-device
+ * gradient (SP blog page, bmjup.com/post/14448.html, FAQ Q1).
+ * o: fp32 device [Tq][Hq][D]; dout: bf16 device, row stride q_row_stride;
+ * hq > 0, d in {64, 128}. Plan tile shape 64 x 128. Errors:
+ * SAP_ERR_INVALID_ARG (NULL or misaligned pointer, bad stride),
+ * SAP_ERR_UNSUPPORTED (shape, or a plan too large for one dispatch),
+ * SAP_ERR_STATE (plan not uploaded), SAP_ERR_HIP (launch failure).
  */
 sap_status sap_attn_bwd_rowterm(sap_plan_t plan, const float *o, const void *dout,
                                 int64_t q_row_stride, int32_t hq, int32_t d,
                                 float *delta, void *hip_stream);
 
 /*
- * sap_attn_bwd_accumulate -- sap_attn_bwd without the row-term pass: the
- * caller passes delta fp32 [Hq][Tq] from sap_attn_bwd_rowterm (it must hold
- * the rows of this plan's touched Q tiles). Same outputs and accumulation
- * rules as sap_attn_bwd. workspace: device, 16-byte aligned,
- * >= sap_attn_bwd_workspace(plan, 0, hkv, d) bytes (may be NULL when that
- * is 0). Plan tile shape 64 x 128.
+ * sap_attn_bwd_accumulate -- sap_attn_bwd without the row-term pass (the
+ * recompute backward of the AutoSP page, gist.science/zh/paper/2604.27089,
+ * section 2.B, for one ring step: its dQ, dK, dV add into the running
+ * gradients, which sum over the steps to the one-device gradient, SP blog
+ * page, bmjup.com/post/14448.html, FAQ Q1). The caller passes delta fp32
+ * [Hq][Tq] from sap_attn_bwd_rowterm (it must hold the rows of this plan's
+ * touched Q tiles). Same outputs, layouts and accumulation rules as
+ * sap_attn_bwd; equals sap_attn_bwd_dkdv followed by sap_attn_bwd_dq.
+ * workspace: device, 16-byte aligned, >= sap_attn_bwd_workspace(plan, 0, hkv,
+ * d) bytes (may be NULL when that is 0); calls sharing one workspace must not
+ * overlap. Plan tile shape 64 x 128. Errors as sap_attn_bwd.
  */
 sap_status sap_attn_bwd_accumulate(sap_plan_t plan, const void *q, const void *k, const void *v,
                                    const float *lse_final, const float *delta, const void *dout,
@@ -270,6 +306,41 @@ sap_status sap_attn_bwd_accumulate(sap_plan_t plan, const void *q, const void *k
                                    int32_t hq, int32_t hkv, int32_t d, float scale,
                                    float *dq, float *dk, float *dv,
                                    void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * sap_attn_bwd_dkdv -- the key-side half of sap_attn_bwd_accumulate: the
+ * KV-major pass (per KV tile, over its partner Q tiles) that adds
+ *   dV += P^T dO,  dK += scale dS^T q
+ * into dk, dv (fp32 device [Tkv][Hkv][D], accumulated), then adds the
+ * workspace slots of split KV tiles in a fixed order. A ring rank returns
+ * dK / dV to the chunks' owners, so computing them first lets that transfer
+ * overlap the dQ pass (the SP blog page's compute / communication overlap,
+ * bmjup.com/post/14448.html, core principles); the maths is that of the
+ * recompute backward (AutoSP page, gist.science/zh/paper/2604.27089,
+ * section 2.B). Arguments as sap_attn_bwd_accumulate without dq; workspace
+ * >= sap_attn_bwd_workspace(plan, 0, hkv, d) bytes. Deterministic.
+ */
+sap_status sap_attn_bwd_dkdv(sap_plan_t plan, const void *q, const void *k, const void *v,
+                             const float *lse_final, const float *delta, const void *dout,
+                             int64_t q_row_stride, int64_t kv_row_stride,
+                             int32_t hq, int32_t hkv, int32_t d, float scale,
+                             float *dk, float *dv, void *workspace, size_t workspace_bytes,
+                             void *hip_stream);
+
+/*
+ * sap_attn_bwd_dq -- the query-side half of sap_attn_bwd_accumulate: the
+ * Q-major pass (per Q tile, over its partner KV tiles) that recomputes
+ * S and dP and adds dQ += scale dS k into dq (fp32 device [Tq][Hq][D],
+ * accumulated). Same recompute backward (AutoSP page,
+ * gist.science/zh/paper/2604.27089, section 2.B). Needs no workspace.
+ * Arguments as sap_attn_bwd_accumulate without dk, dv, workspace.
+ * Deterministic (each workgroup owns its dQ rows).
+ */
+sap_status sap_attn_bwd_dq(sap_plan_t plan, const void *q, const void *k, const void *v,
+                           const float *lse_final, const float *delta, const void *dout,
+                           int64_t q_row_stride, int64_t kv_row_stride,
+                           int32_t hq, int32_t hkv, int32_t d, float scale,
+                           float *dq, void *hip_stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char *sap_last_error(void);

@@ -20,7 +20,7 @@ __all__ = [
     "SapError", "Segment", "PlanStats", "Plan",
     "sap_plan", "sap_plan_upload", "sap_plan_info", "sap_plan_tiles", "sap_plan_q_tiles",
     "sap_plan_free", "sap_balance", "sap_attn_fwd", "sap_attn_fwd_merge", "sap_lse_merge", "sap_attn_bwd_workspace", "sap_attn_bwd",
-    "sap_attn_bwd_rowterm", "sap_attn_bwd_accumulate",
+    "sap_attn_bwd_rowterm", "sap_attn_bwd_accumulate", "sap_attn_bwd_dkdv", "sap_attn_bwd_dq",
     "sap_last_error", "sap_version", "lib_path", "SAP_TILE_FULL", "SAP_TILE_DIAGONAL",
     "SAP_TILE_PARTIAL",
 ]
@@ -84,6 +84,9 @@ _sigs = {
     "sap_attn_bwd_rowterm": ([_P, _P, _P, _i64, _i32, _i32, _P, _P], _i32),
     "sap_attn_bwd_accumulate": ([_P, _P, _P, _P, _P, _P, _P, _i64, _i64, _i32, _i32, _i32, _f32, _P, _P, _P, _P,
                                  _sz, _P], _i32),
+    "sap_attn_bwd_dkdv": ([_P, _P, _P, _P, _P, _P, _P, _i64, _i64, _i32, _i32, _i32, _f32, _P, _P, _P, _sz, _P],
+                          _i32),
+    "sap_attn_bwd_dq": ([_P, _P, _P, _P, _P, _P, _P, _i64, _i64, _i32, _i32, _i32, _f32, _P, _P], _i32),
     "sap_last_error": ([], ctypes.c_char_p),
     "sap_version": ([], _i32),
 }
@@ -248,3 +251,16 @@ def sap_attn_bwd_accumulate(plan: Plan, q, k, v, lse_final, delta, dout, q_row_s
     _check(_lib.sap_attn_bwd_accumulate(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(lse_final), _ptr(delta),
                                         _ptr(dout), q_row_stride, kv_row_stride, hq, hkv, d, scale, _ptr(dq),
                                         _ptr(dk), _ptr(dv), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def sap_attn_bwd_dkdv(plan: Plan, q, k, v, lse_final, delta, dout, q_row_stride: int, kv_row_stride: int, hq: int,
+                      hkv: int, d: int, scale: float, dk, dv, workspace=None, workspace_bytes: int = 0, stream=None):
+    _check(_lib.sap_attn_bwd_dkdv(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(lse_final), _ptr(delta), _ptr(dout),
+                                  q_row_stride, kv_row_stride, hq, hkv, d, scale, _ptr(dk), _ptr(dv), _ptr(workspace),
+                                  workspace_bytes, _stream(stream)))
+
+
+def sap_attn_bwd_dq(plan: Plan, q, k, v, lse_final, delta, dout, q_row_stride: int, kv_row_stride: int, hq: int,
+                    hkv: int, d: int, scale: float, dq, stream=None):
+    _check(_lib.sap_attn_bwd_dq(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(lse_final), _ptr(delta), _ptr(dout),
+                                q_row_stride, kv_row_stride, hq, hkv, d, scale, _ptr(dq), _stream(stream)))

@@ -50,7 +50,8 @@ def _compile(src: str, resource_usage: bool, verbose: bool) -> str:
             cmd += ["-Rpass-analysis=kernel-resource-usage"]
     if verbose:
         print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
+    # run in the build folder, so any temporaries hipcc leaves land there
+    r = subprocess.run(cmd, capture_output=True, text=True, cwd=BUILD)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
     if verbose or resource_usage:
@@ -68,7 +69,7 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
+    r = subprocess.run(cmd, capture_output=True, text=True, cwd=BUILD)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)

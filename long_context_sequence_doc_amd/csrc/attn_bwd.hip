@@ -812,18 +812,12 @@ __global__ __launch_bounds__(128 * NH) void attn_bwd_dq_kernel(BwdParams p) {
 
 }  // namespace
 
-hipError_t launch_bwd_rowterm(const BwdLaunch &a, hipStream_t stream) {
-  if (a.n_touched_q > 65535) return hipErrorInvalidValue;
-  if (a.d % 8 || a.d / 8 > 64) return hipErrorInvalidValue;
-  const int pairs = a.max_q_rows * a.hq, per_block = NT / (a.d / 8);
-  const dim3 grid{static_cast<unsigned>(a.n_touched_q), static_cast<unsigned>((pairs + per_block - 1) / per_block)};
-  hipLaunchKernelGGL(bwd_rowterm_kernel, grid, dim3(NT), 0, stream,
-                     static_cast<const unsigned short *>(a.dout), a.q_row_stride, a.o, a.delta, a.touched_rows,
-                     a.hq, a.d, a.tq);
-  return hipGetLastError();
-}
+namespace {
 
-hipError_t launch_attn_bwd(const BwdLaunch &a, hipStream_t stream) {
+// (row, head) pairs of the row-term kernel per workgroup, and its grid
+int rowterm_per_block(int d) { return NT / (d / 8); }
+
+BwdParams bwd_params(const BwdLaunch &a) {
   BwdParams p;
   p.q = static_cast<const unsigned short *>(a.q);
   p.k = static_cast<const unsigned short *>(a.k);
@@ -846,58 +840,95 @@ hipError_t launch_attn_bwd(const BwdLaunch &a, hipStream_t stream) {
   p.tq = a.tq;
   p.scale = a.scale;
   p.c = a.scale * LOG2E;
-  // dK, dV: KV-major work
-  if (a.n_work > 0) {
-    if (int64_t(a.n_work) * a.hkv > INT32_MAX) return hipErrorInvalidValue;
-    p.work = a.work;
-    p.range = a.range;
-    p.partners = a.partners;
-    p.n_work = a.n_work;
-    const dim3 grid{static_cast<unsigned>(a.n_work * a.hkv)};
-    if (a.d == 128)
-      hipLaunchKernelGGL(attn_bwd_kv_kernel<128>, grid, dim3(NTK), 0, stream, p);
+  return p;
+}
+
+// query heads per dQ workgroup and its workgroup count
+int dq_heads(int group) { return group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1; }
+int64_t dq_blocks(const BwdLaunch &a) {
+  const int group = a.hq / a.hkv;
+  const int64_t slots = (int64_t(a.n_q_work) * a.hkv + NXCD - 1) / NXCD;
+  return slots * NXCD * (group / dq_heads(group));
+}
+
+}  // namespace
+
+const char *bwd_rowterm_limits(const BwdLaunch &a) {
+  if (a.d % 8 || a.d / 8 > 64) return "row terms need d a multiple of 8, at most 512";
+  // a dispatch counts its work-items in 32 bits; the second grid dimension is at most 65535
+  if (int64_t(a.n_touched_q) * NT > int64_t(UINT32_MAX)) return "row-term grid too large (touched Q tiles)";
+  const int64_t by = (int64_t(a.max_q_rows) * a.hq + rowterm_per_block(a.d) - 1) / rowterm_per_block(a.d);
+  if (by > 65535) return "row-term grid too large (Q tile rows x query heads)";
+  return nullptr;
+}
+
+const char *attn_bwd_limits(const BwdLaunch &a) {
+  const int64_t cap = int64_t(UINT32_MAX);
+  if (int64_t(a.n_work) * a.hkv * NTK > cap) return "dK/dV grid too large (KV-tile chunks x KV heads)";
+  if (int64_t(a.n_reduce) * a.hkv * NT > cap) return "split-tile reduce grid too large";
+  if (dq_blocks(a) * 128 * dq_heads(a.hq / a.hkv) > cap) return "dQ grid too large (Q tiles x query heads)";
+  return nullptr;
+}
+
+hipError_t launch_bwd_rowterm(const BwdLaunch &a, hipStream_t stream) {
+  if (bwd_rowterm_limits(a)) return hipErrorInvalidValue;
+  const int pairs = a.max_q_rows * a.hq, per_block = rowterm_per_block(a.d);
+  const dim3 grid{static_cast<unsigned>(a.n_touched_q), static_cast<unsigned>((pairs + per_block - 1) / per_block)};
+  hipLaunchKernelGGL(bwd_rowterm_kernel, grid, dim3(NT), 0, stream,
+                     static_cast<const unsigned short *>(a.dout), a.q_row_stride, a.o, a.delta, a.touched_rows,
+                     a.hq, a.d, a.tq);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_dkdv(const BwdLaunch &a, hipStream_t stream) {
+  if (a.n_work <= 0) return hipSuccess;
+  if (attn_bwd_limits(a)) return hipErrorInvalidValue;
+  BwdParams p = bwd_params(a);
+  p.work = a.work;
+  p.range = a.range;
+  p.partners = a.partners;
+  p.n_work = a.n_work;
+  const dim3 grid{static_cast<unsigned>(a.n_work * a.hkv)};
+  if (a.d == 128)
+    hipLaunchKernelGGL(attn_bwd_kv_kernel<128>, grid, dim3(NTK), 0, stream, p);
+  else
+    hipLaunchKernelGGL(attn_bwd_kv_kernel<64>, grid, dim3(NTK), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.n_reduce > 0) {
+    hipLaunchKernelGGL(bwd_kv_reduce_kernel, dim3(static_cast<unsigned>(a.n_reduce * a.hkv), BNB / RK), dim3(NT), 0,
+                       stream, a.kv_reduce, a.partial, a.n_slots, a.hkv, a.d, a.scale, a.dk, a.dv);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+hipError_t launch_attn_bwd_dq(const BwdLaunch &a, hipStream_t stream) {
+  if (a.n_q_work <= 0) return hipSuccess;
+  if (attn_bwd_limits(a)) return hipErrorInvalidValue;
+  BwdParams p = bwd_params(a);
+  p.work = a.q_work;
+  p.range = a.q_range;
+  p.partners = a.q_partners;
+  p.n_work = a.n_q_work;
+  const int nh = dq_heads(p.group);
+  const dim3 grid{static_cast<unsigned>(dq_blocks(a))};
+  if (a.d == 128) {
+    if (nh == 4)
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 4>), grid, dim3(512), 0, stream, p);
+    else if (nh == 2)
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 2>), grid, dim3(256), 0, stream, p);
     else
-      hipLaunchKernelGGL(attn_bwd_kv_kernel<64>, grid, dim3(NTK), 0, stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (a.n_reduce > 0) {
-      if (int64_t(a.n_reduce) * a.hkv > INT32_MAX) return hipErrorInvalidValue;
-      hipLaunchKernelGGL(bwd_kv_reduce_kernel, dim3(static_cast<unsigned>(a.n_reduce * a.hkv), BNB / RK), dim3(NT), 0, stream,
-                         a.kv_reduce, a.partial, a.n_slots, a.hkv, a.d, a.scale, a.dk, a.dv);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 1>), grid, dim3(128), 0, stream, p);
+  } else {
+    if (nh == 4)
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 4>), grid, dim3(512), 0, stream, p);
+    else if (nh == 2)
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 2>), grid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 1>), grid, dim3(128), 0, stream, p);
   }
-  // dQ: Q-major work
-  if (a.n_q_work > 0) {
-    p.work = a.q_work;
-    p.range = a.q_range;
-    p.partners = a.q_partners;
-    p.n_work = a.n_q_work;
-    const int nh = p.group % 4 == 0 ? 4 : p.group % 2 == 0 ? 2 : 1;   // query heads per workgroup
-    const int64_t slots = (int64_t(a.n_q_work) * a.hkv + NXCD - 1) / NXCD;
-    const int64_t blocks = slots * NXCD * (p.group / nh);
-    if (blocks > INT32_MAX) return hipErrorInvalidValue;
-    const dim3 grid{static_cast<unsigned>(blocks)};
-    if (a.d == 128) {
-      if (nh == 4)
-        hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 4>), grid, dim3(512), 0, stream, p);
-      else if (nh == 2)
-        hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 2>), grid, dim3(256), 0, stream, p);
-      else
-        hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 1>), grid, dim3(128), 0, stream, p);
-    } else {
-      if (nh == 4)
-        hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 4>), grid, dim3(512), 0, stream, p);
-      else if (nh == 2)
-        hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 2>), grid, dim3(256), 0, stream, p);
-      else
-        hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 1>), grid, dim3(128), 0, stream, p);
-    }
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  return hipGetLastError();
 }
 
 }  // namespace sap

@@ -50,6 +50,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdint>
 #include <type_traits>
 
 #include "kernels.h"
@@ -443,18 +444,32 @@ __global__ __launch_bounds__(2 * TM * NH) __attribute__((amdgpu_waves_per_eu(2))
     const float la = *lp;                        // both lanes read before lane hf == 0 writes
     const float mx = fmaxf(la, lb), mn = fminf(la, lb);
     const float L = mx + log1pf(__expf(mn - mx));
-    const float wa = la == -INFINITY ? 0.f : __expf(la - L);
     const float wb = __expf(lb - L) / l;
+    if (la == -INFINITY) {
+      // the running side holds no keys: its O is not read (a select, so
+      // whatever it holds cannot leak into the result)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int ig = 0; ig < 4; ++ig) {
-        const f32x4 a = *reinterpret_cast<const f32x4 *>(op + db * 32 + 8 * ig);
-        f32x4 v4;
+        for (int ig = 0; ig < 4; ++ig) {
+          f32x4 v4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = wa * a[e] + wb * oacc[db][4 * ig + e];
-        *reinterpret_cast<f32x4 *>(op + db * 32 + 8 * ig) = v4;
-      }
+          for (int e = 0; e < 4; ++e) v4[e] = wb * oacc[db][4 * ig + e];
+          *reinterpret_cast<f32x4 *>(op + db * 32 + 8 * ig) = v4;
+        }
+    } else {
+      const float wa = __expf(la - L);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int ig = 0; ig < 4; ++ig) {
+          const f32x4 a = *reinterpret_cast<const f32x4 *>(op + db * 32 + 8 * ig);
+          f32x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = wa * a[e] + wb * oacc[db][4 * ig + e];
+          *reinterpret_cast<f32x4 *>(op + db * 32 + 8 * ig) = v4;
+        }
+    }
     if (hf == 0) *lp = L;
     return;
   }
@@ -475,7 +490,33 @@ __global__ __launch_bounds__(2 * TM * NH) __attribute__((amdgpu_waves_per_eu(2))
 
 }  // namespace
 
+namespace {
+
+// workgroups and threads per workgroup of a forward launch
+void fwd_grid(const FwdLaunch &a, int64_t *blocks, int *threads) {
+  const int group = a.hq / a.hkv;
+  const int nh = a.block_m == 128 && group % 2 == 0 ? 2 : 1;   // query heads per workgroup
+  const int64_t slots = (int64_t(a.n_work) * a.hkv + NXCD - 1) / NXCD;
+  *blocks = slots * NXCD * (group / nh);
+  *threads = 2 * a.block_m * nh;
+}
+
+}  // namespace
+
+const char *attn_fwd_limits(const FwdLaunch &a) {
+  if (a.block_m != 128 && a.block_m != 256) return "forward Q tiles must have 128 or 256 rows";
+  int64_t blocks;
+  int threads;
+  fwd_grid(a, &blocks, &threads);
+  // a dispatch counts its work-items in 32 bits
+  if (blocks * threads > int64_t(UINT32_MAX)) return "forward grid too large (Q tiles x KV heads x head groups)";
+  // K / V row offsets inside a 64-row tile are 32-bit
+  if (a.kv_row_stride > INT32_MAX / BN) return "kv_row_stride too large for 32-bit tile offsets";
+  return nullptr;
+}
+
 hipError_t launch_attn_fwd(const FwdLaunch &a, hipStream_t stream) {
+  if (attn_fwd_limits(a)) return hipErrorInvalidValue;
   FwdParams p;
   p.q = static_cast<const unsigned short *>(a.q);
   p.k = static_cast<const unsigned short *>(a.k);
@@ -500,12 +541,10 @@ hipError_t launch_attn_fwd(const FwdLaunch &a, hipStream_t stream) {
   // 8 waves share each staged K / V tile (4 for 128-row tiles, odd groups).
   const int tm = a.block_m;
   const int nh = tm == 128 && p.group % 2 == 0 ? 2 : 1;   // query heads per workgroup
-  const int64_t slots = (int64_t(p.n_groups) + NXCD - 1) / NXCD;
-  const int64_t blocks = slots * NXCD * (p.group / nh);
-  // 32-bit row offsets inside a 64-row tile
-  if (blocks > INT32_MAX || a.kv_row_stride > INT32_MAX / BN) return hipErrorInvalidValue;
-  if (tm != 128 && tm != 256) return hipErrorInvalidValue;
-  const dim3 grid{static_cast<unsigned>(blocks)}, block{static_cast<unsigned>(2 * tm * nh)};
+  int64_t blocks;
+  int threads;
+  fwd_grid(a, &blocks, &threads);
+  const dim3 grid{static_cast<unsigned>(blocks)}, block{static_cast<unsigned>(threads)};
 #define SAP_FWD_LAUNCH(DD, MM, TT, HH) \
   hipLaunchKernelGGL((attn_fwd_kernel<DD, MM, TT, HH>), grid, block, 0, stream, p)
 #define SAP_FWD_SHAPES(DD, MM)                                   \

@@ -26,6 +26,8 @@ struct FwdLaunch {
 };
 
 hipError_t launch_attn_fwd(const FwdLaunch &a, hipStream_t stream);
+// nullptr if the launch's grid fits the hardware's dispatch limits, else why not
+const char *attn_fwd_limits(const FwdLaunch &a);
 
 struct MergeLaunch {
   float *o_acc, *lse_acc;
@@ -37,6 +39,7 @@ struct MergeLaunch {
 };
 
 hipError_t launch_lse_merge(const MergeLaunch &a, hipStream_t stream);
+const char *lse_merge_limits(const MergeLaunch &a);
 
 struct BwdLaunch {
   const void *q, *k, *v, *dout;
@@ -68,7 +71,11 @@ struct BwdLaunch {
 
 // D_r = dO_r . O_r for the rows of the given tiles
 hipError_t launch_bwd_rowterm(const BwdLaunch &a, hipStream_t stream);
-// dq / dk / dv given a.delta (a KV-major dK/dV kernel, then a Q-major dQ kernel)
-hipError_t launch_attn_bwd(const BwdLaunch &a, hipStream_t stream);
+const char *bwd_rowterm_limits(const BwdLaunch &a);
+// dk / dv given a.delta: the KV-major kernel, then the ordered reduce of split tiles
+hipError_t launch_attn_bwd_dkdv(const BwdLaunch &a, hipStream_t stream);
+// dq given a.delta: the Q-major kernel
+hipError_t launch_attn_bwd_dq(const BwdLaunch &a, hipStream_t stream);
+const char *attn_bwd_limits(const BwdLaunch &a);
 
 }  // namespace sap

@@ -6,7 +6,8 @@
 // rank the full-sequence result (same page, core principles). With partial
 // results over disjoint KV sets given as (O, LSE):
 //     L = ln(e^La + e^Lb),  O = e^(La - L) O_a + e^(Lb - L) O_b
-// A side whose LSE is -inf holds no keys and contributes nothing.
+// A side whose LSE is -inf holds no keys and contributes nothing (its O is
+// not read into the result at all); both -inf leaves O = 0, LSE = -inf.
 //
 // HBM-bound elementwise work: (12 D + 12) bytes per (row, head). A touched Q
 // tile's rows are one contiguous [rows][Hq][D] block of O; D/4 consecutive
@@ -17,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdint>
 
 #include "kernels.h"
 
@@ -70,14 +72,28 @@ __global__ __launch_bounds__(NTHREADS) void lse_merge_kernel(MergeParams p) {
     }
     const int64_t e = int64_t(rh) * D4 + c;
     const f32x4 a = oa[e], b = ob[e];
-    oa[e] = wa * a + wb * b;
+    // a side with LSE = -inf holds no keys: it is dropped by a select, not
+    // multiplied by 0, so whatever its O holds (even NaN) cannot leak in
+    f32x4 m;
+    if (la == -INFINITY)
+      m = lb == -INFINITY ? f32x4{0.f, 0.f, 0.f, 0.f} : wb * b;
+    else
+      m = lb == -INFINITY ? wa * a : wa * a + wb * b;
+    oa[e] = m;
     if (c == 0) p.lse_acc[li] = L;
   }
 }
 
 }  // namespace
 
+const char *lse_merge_limits(const MergeLaunch &a) {
+  if (int64_t(a.max_rows) * a.hq > INT32_MAX / 2) return "merge tile too large (rows x heads)";
+  if (int64_t(a.n_touched) * NTHREADS > int64_t(UINT32_MAX)) return "merge grid too large (touched Q tiles)";
+  return nullptr;
+}
+
 hipError_t launch_lse_merge(const MergeLaunch &a, hipStream_t stream) {
+  if (lse_merge_limits(a)) return hipErrorInvalidValue;
   MergeParams p;
   p.o_acc = a.o_acc;
   p.lse_acc = a.lse_acc;
@@ -88,7 +104,6 @@ hipError_t launch_lse_merge(const MergeLaunch &a, hipStream_t stream) {
   p.hq = a.hq;
   p.single_rows = a.touched_rows ? 0 : a.tq;
   const int64_t pairs = int64_t(a.max_rows) * a.hq;
-  if (pairs > INT32_MAX / 2) return hipErrorInvalidValue;
   const int rh = a.d >= 4 && a.d <= 256 ? NTHREADS / (a.d / 4) : 1;
   int64_t by = (pairs + rh - 1) / rh;
   if (by < 1) by = 1;

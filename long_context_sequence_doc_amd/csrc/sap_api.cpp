@@ -59,7 +59,7 @@ sap_status check_uploaded(sap_plan_t plan) {
 
 extern "C" {
 
-int32_t sap_version(void) { return 200; }
+int32_t sap_version(void) { return 300; }
 
 const char *sap_last_error(void) { return g_last_error.c_str(); }
 
@@ -235,7 +235,6 @@ sap_status fwd_impl(sap_plan_t plan, const void *q, const void *k, const void *v
     return fail(SAP_ERR_UNSUPPORTED, "forward needs a 128 x 64 or 256 x 64 plan");
   if (!(scale > 0.f) || !(scale < 1e30f)) return fail(SAP_ERR_INVALID_ARG, "scale must be positive and finite");
   if (P.q_work.empty()) return ok();
-  if ((s = check_uploaded(plan)) != SAP_OK) return s;
   if (!q || !k || !v || !o || !lse) return fail(SAP_ERR_INVALID_ARG, "NULL tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return fail(SAP_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
@@ -246,10 +245,12 @@ sap_status fwd_impl(sap_plan_t plan, const void *q, const void *k, const void *v
   a.q_row_stride = q_row_stride; a.kv_row_stride = kv_row_stride;
   a.hq = hq; a.hkv = hkv; a.d = d; a.scale = scale;
   a.o = o; a.lse = lse; a.tq = P.tq;
-  a.work = P.dev.q_work; a.range = P.dev.q_range; a.partners = P.dev.q_partners; a.ds_q = P.dev.ds_q;
   a.n_work = int32_t(P.q_work.size());
   a.block_m = P.bm;
   a.merge = merge;
+  if (const char *why = sap::attn_fwd_limits(a)) return fail(SAP_ERR_UNSUPPORTED, why);
+  if ((s = check_uploaded(plan)) != SAP_OK) return s;
+  a.work = P.dev.q_work; a.range = P.dev.q_range; a.partners = P.dev.q_partners; a.ds_q = P.dev.ds_q;
   hipError_t e = sap::launch_attn_fwd(a, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
   return ok();
@@ -292,6 +293,7 @@ sap_status sap_lse_merge(sap_plan_t plan, float *o_acc, float *lse_acc, const fl
   if (!aligned16(o_acc) || !aligned16(o_part)) return fail(SAP_ERR_INVALID_ARG, "O pointers must be 16-byte aligned");
   a.o_acc = o_acc; a.lse_acc = lse_acc; a.o_part = o_part; a.lse_part = lse_part;
   a.tq = tq; a.hq = hq; a.d = d;
+  if (const char *why = sap::lse_merge_limits(a)) return fail(SAP_ERR_UNSUPPORTED, why);
   hipError_t e = sap::launch_lse_merge(a, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "lse_merge launch");
   return ok();
@@ -343,52 +345,90 @@ void fill_bwd(const sap::Plan &P, sap::BwdLaunch *a) {
   a->ds_q = P.dev.ds_q;
 }
 
-sap_status rowterm_impl(sap_plan_t plan, const float *o, const void *dout, int64_t q_row_stride, int32_t hq,
-                        int32_t d, float *delta, hipStream_t stream) {
+// Checks of the row-term pass; fills *a. Launches nothing.
+sap_status rowterm_check(sap_plan_t plan, const float *o, const void *dout, int64_t q_row_stride, int32_t hq,
+                         int32_t d, float *delta, sap::BwdLaunch *a) {
   const sap::Plan &P = plan->p;
-  if (P.touched.empty()) return ok();
-  sap_status s = check_uploaded(plan);
-  if (s != SAP_OK) return s;
   if (!o || !dout || !delta) return fail(SAP_ERR_INVALID_ARG, "NULL pointer");
   if (!aligned16(o) || !aligned16(dout) || !aligned16(delta)) return fail(SAP_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
   if (q_row_stride < int64_t(hq) * d || q_row_stride % 8) return fail(SAP_ERR_INVALID_ARG, "q_row_stride must be >= hq*d and a multiple of 8");
-  sap::BwdLaunch a{};
-  a.o = o; a.dout = dout; a.q_row_stride = q_row_stride; a.hq = hq; a.d = d; a.delta = delta;
-  fill_bwd(P, &a);
-  hipError_t e = sap::launch_bwd_rowterm(a, stream);
-  if (e != hipSuccess) return hip_fail(e, "bwd row-term launch");
+  *a = sap::BwdLaunch{};
+  a->o = o; a->dout = dout; a->q_row_stride = q_row_stride; a->hq = hq; a->d = d; a->delta = delta;
+  fill_bwd(P, a);
+  if (const char *why = sap::bwd_rowterm_limits(*a)) return fail(SAP_ERR_UNSUPPORTED, why);
+  const sap_status s = check_uploaded(plan);
+  if (s != SAP_OK) return s;
+  fill_bwd(P, a);          // the device tables' addresses, now that they exist
   return SAP_OK;
 }
 
-sap_status accumulate_impl(sap_plan_t plan, const void *q, const void *k, const void *v, const float *lse_final,
-                           const float *delta, const void *dout, int64_t q_row_stride, int64_t kv_row_stride,
-                           int32_t hq, int32_t hkv, int32_t d, float scale, float *dq, float *dk, float *dv,
-                           float *partial, size_t partial_avail, hipStream_t stream) {
+// Which passes of the backward a call runs.
+enum BwdPasses { kDkDv = 1, kDq = 2, kBoth = 3 };
+
+// Checks of the dK/dV and / or dQ passes; fills *a. Launches nothing.
+sap_status accumulate_check(sap_plan_t plan, const void *q, const void *k, const void *v, const float *lse_final,
+                            const float *delta, const void *dout, int64_t q_row_stride, int64_t kv_row_stride,
+                            int32_t hq, int32_t hkv, int32_t d, float scale, float *dq, float *dk, float *dv,
+                            float *partial, size_t partial_avail, int passes, sap::BwdLaunch *a) {
   const sap::Plan &P = plan->p;
   if (!(scale > 0.f) || !(scale < 1e30f)) return fail(SAP_ERR_INVALID_ARG, "scale must be positive and finite");
-  if (P.kv_work.empty()) return ok();
-  sap_status s = check_uploaded(plan);
-  if (s != SAP_OK) return s;
-  const size_t need = partial_bytes(P, hkv, d);
-  if (need > 0 && (!partial || partial_avail < need))
-    return fail(SAP_ERR_INVALID_ARG, "workspace too small (see sap_attn_bwd_workspace)");
-  if (partial && !aligned16(partial)) return fail(SAP_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  if (!q || !k || !v || !lse_final || !delta || !dout || !dq || !dk || !dv) return fail(SAP_ERR_INVALID_ARG, "NULL pointer");
-  const void *ptrs[] = {q, k, v, lse_final, delta, dout, dq, dk, dv};
+  if (passes & kDkDv) {
+    const size_t need = partial_bytes(P, hkv, d);
+    if (need > 0 && (!partial || partial_avail < need))
+      return fail(SAP_ERR_INVALID_ARG, "workspace too small (see sap_attn_bwd_workspace)");
+    if (partial && !aligned16(partial)) return fail(SAP_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    if (!dk || !dv || !aligned16(dk) || !aligned16(dv)) return fail(SAP_ERR_INVALID_ARG, "dk / dv must be 16-byte aligned device pointers");
+  }
+  if ((passes & kDq) && (!dq || !aligned16(dq))) return fail(SAP_ERR_INVALID_ARG, "dq must be a 16-byte aligned device pointer");
+  if (!q || !k || !v || !lse_final || !delta || !dout) return fail(SAP_ERR_INVALID_ARG, "NULL pointer");
+  const void *ptrs[] = {q, k, v, lse_final, delta, dout};
   for (const void *p : ptrs)
     if (!aligned16(p)) return fail(SAP_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
   if (q_row_stride < int64_t(hq) * d || q_row_stride % 8) return fail(SAP_ERR_INVALID_ARG, "q_row_stride must be >= hq*d and a multiple of 8");
   if (kv_row_stride < int64_t(hkv) * d || kv_row_stride % 8) return fail(SAP_ERR_INVALID_ARG, "kv_row_stride must be >= hkv*d and a multiple of 8");
-  sap::BwdLaunch a{};
-  a.q = q; a.k = k; a.v = v; a.dout = dout; a.lse = lse_final; a.delta = const_cast<float *>(delta);
-  a.q_row_stride = q_row_stride; a.kv_row_stride = kv_row_stride;
-  a.hq = hq; a.hkv = hkv; a.d = d; a.scale = scale;
-  a.dq = dq; a.dk = dk; a.dv = dv;
-  a.partial = partial;
-  fill_bwd(P, &a);
-  hipError_t e = sap::launch_attn_bwd(a, stream);
-  if (e != hipSuccess) return hip_fail(e, "attn_bwd launch");
+  *a = sap::BwdLaunch{};
+  a->q = q; a->k = k; a->v = v; a->dout = dout; a->lse = lse_final; a->delta = const_cast<float *>(delta);
+  a->q_row_stride = q_row_stride; a->kv_row_stride = kv_row_stride;
+  a->hq = hq; a->hkv = hkv; a->d = d; a->scale = scale;
+  a->dq = dq; a->dk = dk; a->dv = dv;
+  a->partial = partial;
+  fill_bwd(P, a);
+  if (const char *why = sap::attn_bwd_limits(*a)) return fail(SAP_ERR_UNSUPPORTED, why);
+  const sap_status s = check_uploaded(plan);
+  if (s != SAP_OK) return s;
+  fill_bwd(P, a);          // the device tables' addresses, now that they exist
   return SAP_OK;
+}
+
+sap_status accumulate_launch(const sap::BwdLaunch &a, int passes, hipStream_t stream) {
+  if (passes & kDkDv) {
+    const hipError_t e = sap::launch_attn_bwd_dkdv(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "attn_bwd dK/dV launch");
+  }
+  if (passes & kDq) {
+    const hipError_t e = sap::launch_attn_bwd_dq(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "attn_bwd dQ launch");
+  }
+  return SAP_OK;
+}
+
+sap_status accumulate_entry(sap_plan_t plan, const void *q, const void *k, const void *v, const float *lse_final,
+                            const float *delta, const void *dout, int64_t q_row_stride, int64_t kv_row_stride,
+                            int32_t hq, int32_t hkv, int32_t d, float scale, float *dq, float *dk, float *dv,
+                            void *workspace, size_t workspace_bytes, int passes, void *hip_stream) {
+  sap_status s = check_bwd_common(plan, hq, hkv, d);
+  if (s != SAP_OK) return s;
+  if (plan->p.kv_work.empty()) {
+    if (!(scale > 0.f) || !(scale < 1e30f)) return fail(SAP_ERR_INVALID_ARG, "scale must be positive and finite");
+    return ok();
+  }
+  sap::BwdLaunch a;
+  if ((s = accumulate_check(plan, q, k, v, lse_final, delta, dout, q_row_stride, kv_row_stride, hq, hkv, d, scale,
+                            dq, dk, dv, static_cast<float *>(workspace), workspace ? workspace_bytes : 0, passes,
+                            &a)) != SAP_OK)
+    return s;
+  if ((s = accumulate_launch(a, passes, static_cast<hipStream_t>(hip_stream))) != SAP_OK) return s;
+  return ok();
 }
 
 }  // namespace
@@ -397,8 +437,11 @@ sap_status sap_attn_bwd_rowterm(sap_plan_t plan, const float *o, const void *dou
                                 int32_t hq, int32_t d, float *delta, void *hip_stream) {
   sap_status s = check_bwd_common(plan, hq, 1, d);
   if (s != SAP_OK) return s;
-  if ((s = rowterm_impl(plan, o, dout, q_row_stride, hq, d, delta, static_cast<hipStream_t>(hip_stream))) != SAP_OK)
-    return s;
+  if (plan->p.touched.empty()) return ok();
+  sap::BwdLaunch a;
+  if ((s = rowterm_check(plan, o, dout, q_row_stride, hq, d, delta, &a)) != SAP_OK) return s;
+  const hipError_t e = sap::launch_bwd_rowterm(a, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "bwd row-term launch");
   return ok();
 }
 
@@ -407,13 +450,23 @@ sap_status sap_attn_bwd_accumulate(sap_plan_t plan, const void *q, const void *k
                                    int64_t q_row_stride, int64_t kv_row_stride, int32_t hq, int32_t hkv,
                                    int32_t d, float scale, float *dq, float *dk, float *dv, void *workspace,
                                    size_t workspace_bytes, void *hip_stream) {
-  sap_status s = check_bwd_common(plan, hq, hkv, d);
-  if (s != SAP_OK) return s;
-  if ((s = accumulate_impl(plan, q, k, v, lse_final, delta, dout, q_row_stride, kv_row_stride, hq, hkv, d, scale,
-                           dq, dk, dv, static_cast<float *>(workspace), workspace ? workspace_bytes : 0,
-                           static_cast<hipStream_t>(hip_stream))) != SAP_OK)
-    return s;
-  return ok();
+  return accumulate_entry(plan, q, k, v, lse_final, delta, dout, q_row_stride, kv_row_stride, hq, hkv, d, scale, dq,
+                          dk, dv, workspace, workspace_bytes, kBoth, hip_stream);
+}
+
+sap_status sap_attn_bwd_dkdv(sap_plan_t plan, const void *q, const void *k, const void *v, const float *lse_final,
+                             const float *delta, const void *dout, int64_t q_row_stride, int64_t kv_row_stride,
+                             int32_t hq, int32_t hkv, int32_t d, float scale, float *dk, float *dv, void *workspace,
+                             size_t workspace_bytes, void *hip_stream) {
+  return accumulate_entry(plan, q, k, v, lse_final, delta, dout, q_row_stride, kv_row_stride, hq, hkv, d, scale,
+                          nullptr, dk, dv, workspace, workspace_bytes, kDkDv, hip_stream);
+}
+
+sap_status sap_attn_bwd_dq(sap_plan_t plan, const void *q, const void *k, const void *v, const float *lse_final,
+                           const float *delta, const void *dout, int64_t q_row_stride, int64_t kv_row_stride,
+                           int32_t hq, int32_t hkv, int32_t d, float scale, float *dq, void *hip_stream) {
+  return accumulate_entry(plan, q, k, v, lse_final, delta, dout, q_row_stride, kv_row_stride, hq, hkv, d, scale, dq,
+                          nullptr, nullptr, nullptr, 0, kDq, hip_stream);
 }
 
 sap_status sap_attn_bwd(sap_plan_t plan, const void *q, const void *k, const void *v, const float *o,
@@ -428,15 +481,19 @@ sap_status sap_attn_bwd(sap_plan_t plan, const void *q, const void *k, const voi
   if (!workspace) return fail(SAP_ERR_INVALID_ARG, "workspace is NULL");
   if (workspace_bytes < sap_attn_bwd_workspace(plan, hq, hkv, d)) return fail(SAP_ERR_INVALID_ARG, "workspace too small");
   if (!aligned16(workspace)) return fail(SAP_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  if (!o) return fail(SAP_ERR_INVALID_ARG, "NULL pointer");
-  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   float *delta = static_cast<float *>(workspace);
   const size_t delta_bytes = sap_attn_bwd_workspace(plan, hq, hkv, d) - sap_attn_bwd_workspace(plan, 0, hkv, d);
   float *partial = reinterpret_cast<float *>(static_cast<char *>(workspace) + delta_bytes);
-  if ((s = rowterm_impl(plan, o, dout, q_row_stride, hq, d, delta, stream)) != SAP_OK) return s;
-  if ((s = accumulate_impl(plan, q, k, v, lse_final, delta, dout, q_row_stride, kv_row_stride, hq, hkv, d, scale,
-                           dq, dk, dv, partial, workspace_bytes - delta_bytes, stream)) != SAP_OK)
+  // every check of both passes before anything is launched
+  sap::BwdLaunch ra, ba;
+  if ((s = rowterm_check(plan, o, dout, q_row_stride, hq, d, delta, &ra)) != SAP_OK) return s;
+  if ((s = accumulate_check(plan, q, k, v, lse_final, delta, dout, q_row_stride, kv_row_stride, hq, hkv, d, scale,
+                            dq, dk, dv, partial, workspace_bytes - delta_bytes, kBoth, &ba)) != SAP_OK)
     return s;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const hipError_t e = sap::launch_bwd_rowterm(ra, stream);
+  if (e != hipSuccess) return hip_fail(e, "bwd row-term launch");
+  if ((s = accumulate_launch(ba, kBoth, stream)) != SAP_OK) return s;
   return ok();
 }
 

@@ -34,9 +34,9 @@ from typing import List, Sequence, Tuple
 
 import torch
 
-from . import (sap_attn_bwd_accumulate, sap_attn_bwd_rowterm, sap_attn_bwd_workspace, sap_attn_fwd,
-               sap_attn_fwd_merge, sap_lse_merge, sap_plan, sap_plan_free, sap_plan_info, sap_plan_q_tiles,
-               sap_plan_upload)
+from . import (sap_attn_bwd_accumulate, sap_attn_bwd_dkdv, sap_attn_bwd_dq, sap_attn_bwd_rowterm,
+               sap_attn_bwd_workspace, sap_attn_fwd, sap_attn_fwd_merge, sap_lse_merge, sap_plan, sap_plan_free,
+               sap_plan_info, sap_plan_q_tiles, sap_plan_upload)
 
 BLOCK_M, BLOCK_N = 128, 64
 N_CU = 256
@@ -188,6 +188,16 @@ class RankBackward:
                    stream=None):
         sap_attn_bwd_accumulate(self.plans[i], q, k, v, lse, self.delta, dout, q_row_stride, kv_row_stride,
                                 self.hq, self.hkv, self.d, self.scale, dq, dk, dv, self.ws, self.ws_bytes, stream)
+
+    def dkdv(self, i: int, q, k, v, lse, dout, q_row_stride: int, kv_row_stride: int, dk, dv, stream=None):
+        """Step i's dK / dV pass alone (the first half of ``accumulate``)."""
+        sap_attn_bwd_dkdv(self.plans[i], q, k, v, lse, self.delta, dout, q_row_stride, kv_row_stride, self.hq,
+                          self.hkv, self.d, self.scale, dk, dv, self.ws, self.ws_bytes, stream)
+
+    def dq(self, i: int, q, k, v, lse, dout, q_row_stride: int, kv_row_stride: int, dq, stream=None):
+        """Step i's dQ pass alone (the second half of ``accumulate``)."""
+        sap_attn_bwd_dq(self.plans[i], q, k, v, lse, self.delta, dout, q_row_stride, kv_row_stride, self.hq,
+                        self.hkv, self.d, self.scale, dq, stream)
 
     def run(self, q, k, v, o, lse, dout, q_row_stride: int, kv_row_stride: int, dq, dk, dv, stream=None):
         self.rowterm(o, dout, q_row_stride, stream)

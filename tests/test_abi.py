@@ -113,3 +113,55 @@ def test_bwd_split_workspace():
     # chunks of max(8, ceil(2048 / 128)) = 16 partners: 4 per KV tile
     assert slots == 32 * 4
     assert sap.sap_attn_bwd_workspace(big, 3, 2, 64) >= ws + 3 * 4096 * 4
+
+
+def test_grid_limits_are_refused_before_launch():
+    """Calls whose grid would not fit one dispatch (work-items counted in 32
+    bits, a second grid dimension of at most 65535) are refused on the host
+    with SAP_ERR_UNSUPPORTED before any launch -- here on plans that were
+    never uploaded, so nothing could have reached a GPU."""
+    pb = _plan(bm=64, bn=128)
+    hq = 16384                      # row terms: 4 * hq workgroups in the second grid dimension
+    with pytest.raises(sap.SapError) as e:
+        sap.sap_attn_bwd_rowterm(pb, 16, 16, hq * 128, hq, 128, 16, stream=0)
+    assert e.value.status == sap.SAP_ERR_UNSUPPORTED and "row-term grid" in str(e.value)
+    with pytest.raises(sap.SapError) as e:
+        sap.sap_attn_bwd(pb, 16, 16, 16, 16, 16, 16, hq * 128, 128, hq, 1, 128, 0.1, 16, 16, 16, 16, 1 << 40,
+                         stream=0)
+    assert e.value.status == sap.SAP_ERR_UNSUPPORTED
+    # one fewer head fits: the host checks pass and the call stops at the upload check
+    with pytest.raises(sap.SapError) as e:
+        sap.sap_attn_bwd_rowterm(pb, 16, 16, (hq - 1) * 128, hq - 1, 128, 16, stream=0)
+    assert e.value.status == sap.SAP_ERR_STATE
+    # the forward: 2^22 query heads over one KV head need more than 2^32 work-items
+    pf = _plan()
+    big = 1 << 22
+    with pytest.raises(sap.SapError) as e:
+        sap.sap_attn_fwd(pf, 16, 16, 16, big * 64, 64, big, 1, 64, 0.1, 16, 16, stream=0)
+    assert e.value.status == sap.SAP_ERR_UNSUPPORTED and "forward grid" in str(e.value)
+
+
+def test_backward_halves_validate_before_launch():
+    """sap_attn_bwd_dkdv / sap_attn_bwd_dq check their arguments like the
+    whole backward: wrong tile shape, bad strides, missing outputs, plan not
+    uploaded."""
+    pf = _plan()
+    with pytest.raises(sap.SapError) as e:
+        sap.sap_attn_bwd_dkdv(pf, 16, 16, 16, 16, 16, 16, 128, 128, 2, 2, 64, 0.1, 16, 16, stream=0)
+    assert e.value.status == sap.SAP_ERR_UNSUPPORTED
+    pb = _plan(bm=64, bn=128)
+    with pytest.raises(sap.SapError) as e:
+        sap.sap_attn_bwd_dq(pb, 16, 16, 16, 16, 16, 16, 100, 128, 2, 2, 64, 0.1, 16, stream=0)
+    assert e.value.status == sap.SAP_ERR_INVALID_ARG and "q_row_stride" in str(e.value)
+    with pytest.raises(sap.SapError) as e:
+        sap.sap_attn_bwd_dq(pb, 16, 16, 16, 16, 16, 16, 128, 128, 2, 2, 64, 0.1, None, stream=0)
+    assert e.value.status == sap.SAP_ERR_INVALID_ARG
+    with pytest.raises(sap.SapError) as e:
+        sap.sap_attn_bwd_dkdv(pb, 16, 16, 16, 16, 16, 16, 128, 128, 2, 2, 64, 0.1, 16, None, stream=0)
+    assert e.value.status == sap.SAP_ERR_INVALID_ARG
+    with pytest.raises(sap.SapError) as e:
+        sap.sap_attn_bwd_dkdv(pb, 16, 16, 16, 16, 16, 16, 128, 128, 2, 2, 64, 0.1, 16, 16, stream=0)
+    assert e.value.status == sap.SAP_ERR_STATE
+    with pytest.raises(sap.SapError) as e:
+        sap.sap_attn_bwd_dq(pb, 16, 16, 16, 16, 16, 16, 128, 128, 2, 2, 64, 0.1, 16, stream=0)
+    assert e.value.status == sap.SAP_ERR_STATE
