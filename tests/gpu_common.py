@@ -60,6 +60,23 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, rows=None, label=""):
     return eo, el
 
 
+def ulysses_rows(cu, n_long: int = 2, tail: int = 256, n_random: int = 4096, seed: int = 5) -> np.ndarray:
+    """The full-size sample of the 512K Ulysses shard: every row of every
+    short document, and the last ``tail`` rows plus ``n_random`` seeded rows
+    of each of the ``n_long`` long documents (rows are independent in the
+    forward, so each sampled row is checked exactly)."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for i in range(len(cu) - 1):
+        s, e = int(cu[i]), int(cu[i + 1])
+        if i < n_long:
+            rows.update(range(max(s, e - tail), e))
+            rows.update(rng.integers(s, e, size=n_random).tolist())
+        else:
+            rows.update(range(s, e))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
 def sample_rows(q_global: np.ndarray, cu: np.ndarray, n_random: int = 256, seed: int = 5) -> np.ndarray:
     """Local rows to check at full size: rows at and next to every document
     start inside the shard, both ends of every 128-row tile, and seeded
@@ -77,3 +94,64 @@ def sample_rows(q_global: np.ndarray, cu: np.ndarray, n_random: int = 256, seed:
     rows.update(rng.integers(0, tq, size=min(n_random, tq)).tolist())
     rows = np.array(sorted(r for r in rows if q_global[r] >= 0), dtype=np.int64)
     return rows
+
+
+def oracle_workers() -> int:
+    """Threads for running the oracle on independent pieces at once: the
+    host's cores, at most 16 (a GPU machine's share)."""
+    import os
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def par_map(fn, items, label=""):
+    """fn over items on a thread pool with one BLAS thread per worker (NumPy
+    releases the GIL inside its matrix products and ufunc loops, so the
+    oracle's pieces run in parallel). Returns the results in order and says
+    how far it got, so a long oracle run is visibly alive."""
+    import contextlib
+    import time
+    from concurrent.futures import ThreadPoolExecutor, as_completed
+    try:
+        from threadpoolctl import threadpool_limits
+        blas_one = threadpool_limits(limits=1, user_api="blas")
+    except Exception:
+        blas_one = contextlib.nullcontext()
+    t0 = last = time.perf_counter()
+    out = [None] * len(items)
+    with blas_one, ThreadPoolExecutor(max_workers=oracle_workers()) as ex:
+        futs = {ex.submit(fn, it): i for i, it in enumerate(items)}
+        done = 0
+        for f in as_completed(futs):
+            out[futs[f]] = f.result()
+            done += 1
+            now = time.perf_counter()
+            if label and (done == len(items) or now - last >= 10.0):
+                last = now
+                say(f"  oracle {label}: {done}/{len(items)} pieces, {now - t0:.1f} s")
+    return out
+
+
+def oracle_forward_rows(q, k, v, gq, gk, cu, scale, rows, label="", piece=256):
+    """The oracle forward on the given local Q rows only (each row is
+    independent, so computing them in pieces is exact): returns O [len(rows),
+    Hq, D] and LSE [Hq, len(rows)] in the order of ``rows``. q, k, v may be
+    bf16 bit patterns (uint16) or floats."""
+    from oracle import attention as A
+    rows = np.asarray(rows, dtype=np.int64)
+    conv = lambda x: f64(x) if x.dtype == np.uint16 else np.asarray(x, dtype=np.float64)
+    k64, v64 = conv(k), conv(v)
+    gq = np.asarray(gq, dtype=np.int64)
+    pieces = [rows[i:i + piece] for i in range(0, len(rows), piece)]
+
+    def one(rs):
+        return A.forward(conv(q[rs]), k64, v64, gq[rs], gk, cu, scale)
+
+    res = par_map(one, pieces, label)
+    if not res:
+        hq, d = q.shape[1], q.shape[2]
+        return np.zeros((0, hq, d)), np.zeros((hq, 0))
+    return np.concatenate([r[0] for r in res], axis=0), np.concatenate([r[1] for r in res], axis=1)

@@ -12,7 +12,7 @@ import pytest
 
 import workloads as W
 from oracle import attention as A
-from tests.gpu_common import TOL_O, f64, need_gpu, say, tensors, to_dev
+from tests.gpu_common import TOL_O, f64, need_gpu, par_map, say, tensors, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -108,11 +108,15 @@ def test_random_small_layouts(seed):
     assert (dq.cpu().numpy()[~vq] == 0).all() and (dk.cpu().numpy()[~vk] == 0).all()
 
 
-@pytest.mark.parametrize("case", [(2, 1, 128, [4096]), (1, 1, 64, [3000, 1096]), (4, 2, 128, [1500, 2596])])
+@pytest.mark.parametrize("case", [(2, 1, 128, [4096]), (1, 1, 64, [3000, 1096]), (4, 2, 128, [1500, 2596]),
+                                  (8, 2, 64, [2500, 1, 1595]), (4, 1, 64, [4096])])
 def test_split_kv_tiles_all_rows(case):
     """Documents long enough that KV tiles meet more partner Q tiles than one
     workgroup takes: their chunks leave partial sums in workspace slots and
-    the ordered reduce adds them. Every dQ, dK, dV row against the oracle."""
+    the ordered reduce adds them. Every dQ, dK, dV row against the oracle.
+    GQA groups of 1, 2 and 4 at both head dims between them, so every
+    compiled dQ workgroup shape (one, two and four query heads) and both
+    dK / dV kernels run."""
     sap = _sap()
     import torch
     hq, hkv, d, lengths = case
@@ -143,6 +147,75 @@ def test_split_kv_tiles_all_rows(case):
     _check("dQ split", dq.cpu().numpy(), dq_ref)
     _check("dK split", dk.cpu().numpy(), dk_ref)
     _check("dV split", dv.cpu().numpy(), dv_ref)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(4, 2, 128), (8, 2, 64)])
+def test_backward_is_deterministic_and_halves_compose(hq, hkv, d):
+    """sap_attn_bwd twice into zeroed buffers on a plan that splits KV tiles:
+    bit-identical dQ, dK, dV (the split tiles' slots are added in a fixed
+    order, no atomics). Then the parts -- sap_attn_bwd_rowterm,
+    sap_attn_bwd_dkdv, sap_attn_bwd_dq -- give the same bits as the one call,
+    and sap_attn_bwd_dkdv leaves dQ alone, sap_attn_bwd_dq dK / dV."""
+    sap = _sap()
+    import torch
+    lengths = [3000, 7, 1089]
+    cu = W.cu_seqlens(lengths)
+    total = int(cu[-1])
+    scale = 1.0 / np.sqrt(d)
+    say(f"case bwd determinism hq={hq} hkv={hkv} d={d} docs={lengths}")
+    rs = np.random.default_rng(61 + d)
+    mk = lambda h: W.bf16_round(rs.standard_normal((total, h, d), dtype=np.float32))
+    qb, kb, vb, dob = mk(hq), mk(hkv), mk(hkv), mk(hq)
+    segs = [(0, total, 0)]
+    plan = sap.sap_plan(cu, segs, segs, 64, 128)
+    sap.sap_plan_upload(plan)
+    ws_all = sap.sap_attn_bwd_workspace(plan, hq, hkv, d)
+    ws_kv = sap.sap_attn_bwd_workspace(plan, 0, hkv, d)
+    assert ws_kv > 0, "the plan must split some KV tile"
+    qd, kd, vd, dod = to_dev(qb), to_dev(kb), to_dev(vb), to_dev(dob)
+    # the final O / LSE from the GPU forward (a training step's inputs)
+    fplan = sap.sap_plan(cu, segs, segs, 128, 64)
+    sap.sap_plan_upload(fplan)
+    o = torch.empty((total, hq, d), device="cuda")
+    lse = torch.empty((hq, total), device="cuda")
+    sap.sap_attn_fwd(fplan, qd, kd, vd, qd.stride(0), kd.stride(0), hq, hkv, d, scale, o, lse)
+    ws = torch.empty(ws_all // 4 + 64, dtype=torch.float32, device="cuda")
+    outs = []
+    for rep in range(2):
+        dq = torch.zeros((total, hq, d), device="cuda")
+        dk = torch.zeros((total, hkv, d), device="cuda")
+        dv = torch.zeros((total, hkv, d), device="cuda")
+        ws.fill_(float("nan") if rep else 7.0)   # workspace contents on entry do not matter
+        sap.sap_attn_bwd(plan, qd, kd, vd, o, lse, dod, qd.stride(0), kd.stride(0), hq, hkv, d, scale, dq, dk, dv,
+                         ws, ws.numel() * 4)
+        torch.cuda.synchronize()
+        outs.append((dq, dk, dv))
+    for a, b, name in zip(outs[0], outs[1], ("dQ", "dK", "dV")):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"{name} differs between two runs"
+    # the parts, into fresh zeroed buffers
+    delta = torch.empty((hq, total), device="cuda")
+    dq = torch.zeros((total, hq, d), device="cuda")
+    dk = torch.zeros((total, hkv, d), device="cuda")
+    dv = torch.zeros((total, hkv, d), device="cuda")
+    part = torch.empty(ws_kv // 4 + 64, dtype=torch.float32, device="cuda")
+    sap.sap_attn_bwd_rowterm(plan, o, dod, dod.stride(0), hq, d, delta)
+    sap.sap_attn_bwd_dkdv(plan, qd, kd, vd, lse, delta, dod, qd.stride(0), kd.stride(0), hq, hkv, d, scale, dk, dv,
+                          part, part.numel() * 4)
+    torch.cuda.synchronize()
+    assert not dq.any(), "the dK/dV pass wrote dQ"
+    sap.sap_attn_bwd_dq(plan, qd, kd, vd, lse, delta, dod, qd.stride(0), kd.stride(0), hq, hkv, d, scale, dq)
+    torch.cuda.synchronize()
+    for a, b, name in zip(outs[0], (dq, dk, dv), ("dQ", "dK", "dV")):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"{name}: parts differ from the one call"
+    # and the values against the oracle (every row)
+    g = np.arange(total)
+    o_ref, lse_ref = A.forward(f64(qb), f64(kb), f64(vb), g, g, cu, scale)
+    dq_ref, dk_ref, dv_ref = A.backward(f64(qb), f64(kb), f64(vb), f64(dob), o_ref, lse_ref, g, g, cu, scale)
+    _check("dQ det", dq.cpu().numpy(), dq_ref)
+    _check("dK det", dk.cpu().numpy(), dk_ref)
+    _check("dV det", dv.cpu().numpy(), dv_ref)
+    sap.sap_plan_free(plan)
+    sap.sap_plan_free(fplan)
 
 
 def test_ring_steps_accumulate_to_full_gradient():
@@ -219,8 +292,13 @@ def test_training_fwd_bwd_sampled():
         pick.update((s0, min(w.total - 1, s0 + 1)))
     pick.update(range(w.total - 8, w.total))
     rows = np.array(sorted(pick))
-    # dK/dV rows: the last 3 keys of every document, so only a few queries see them
-    cols = np.array(sorted({c for e in cu[1:].tolist() for c in range(max(0, e - 3), e)}))
+    # dK/dV rows: the last 3 keys of every document (seen by a few queries
+    # only), every document's first two keys (seen by every query of the
+    # document, through its long unmasked partner lists) and seeded keys
+    cols = {c for e in cu[1:].tolist() for c in range(max(0, e - 3), e)}
+    cols.update(c for s0 in cu[:-1].tolist() for c in (s0, s0 + 1) if c < w.total)
+    cols.update(rng.integers(0, w.total, size=64).tolist())
+    cols = np.array(sorted(cols))
     # the oracle's own forward, on every query row those gradients depend on
     need = set(rows.tolist())
     for c in cols.tolist():
@@ -236,10 +314,33 @@ def test_training_fwd_bwd_sampled():
     rf.close()
 
 
+def _heaviest_kv_tile_keys(rb, step_kv_segs):
+    """Local rows of the KV tile with the most partner Q tiles over the
+    backward's plans, and that count. The planner splits a KV tile into
+    chunks of at most max(8, ceil(n_tiles / 128)) partners; the tile found
+    here is asserted to be split, so its keys' dK / dV go through the
+    workspace slots and the ordered reduce."""
+    import long_context_sequence_doc_amd as sap
+    from oracle import planner as PL
+    best, keys, per = -1, [], 0
+    for i in rb.active:
+        _, kt, _ = sap.sap_plan_tiles(rb.plans[i])
+        cnt = np.bincount(kt)
+        t = int(cnt.argmax())
+        if cnt[t] > best:
+            ls, nr, _ = PL.tiles_of(step_kv_segs[i], 128)[t]
+            best, keys, per = int(cnt[t]), list(range(ls, ls + nr)), max(8, -(-len(kt) // 128))
+    assert best > per, "the heaviest KV tile is not split"
+    return best, keys
+
+
 def _rank_fwd_bwd_sampled(w, label, active=None, two_calls=False):
     """Forward over the ring steps with merges, row terms once, backward per
-    non-empty step; sampled dQ rows and dK/dV rows of KV head 0 against the
-    oracle's own forward/backward."""
+    non-empty step. dQ on sampled rows (all heads); dK / dV on all KV heads
+    at sampled keys: seeded keys of every non-empty step's chunks, each
+    chunk's ends, every document start (the keys the most queries see) and
+    every key of the backward plans' heaviest KV tile (split into chunks).
+    The oracle runs its own forward for the final O / LSE."""
     import torch
     from long_context_sequence_doc_amd.rank import RankBackward, RankForward
     t = tensors("zigzag", True)
@@ -247,9 +348,11 @@ def _rank_fwd_bwd_sampled(w, label, active=None, two_calls=False):
     if two_calls:
         rf = RankForward.local_then_remote(w.cu, w.q_segs, steps, w.hq, w.hkv, w.d, w.scale)
         rb = RankBackward.local_then_remote(w.cu, w.q_segs, steps, w.hq, w.hkv, w.d, w.scale)
+        bwd_steps = [steps[0], [seg for segs in steps[1:] for seg in segs]]
     else:
         rf = RankForward(w.cu, w.q_segs, steps, w.hq, w.hkv, w.d, w.scale)
         rb = RankBackward(w.cu, w.q_segs, steps, w.hq, w.hkv, w.d, w.scale)
+        bwd_steps = steps
     if active is not None:
         assert rb.active == active
     ql, dol = W.local_rows(t.q, w.q_segs), W.local_rows(t.do, w.q_segs)
@@ -260,6 +363,10 @@ def _rank_fwd_bwd_sampled(w, label, active=None, two_calls=False):
     dv = torch.zeros_like(dk)
     rb.run(qd, kd, vd, o, lse, dod, qd.stride(0), kd.stride(0), dq, dk, dv)
     torch.cuda.synchronize()
+    heavy_n, heavy = _heaviest_kv_tile_keys(rb, bwd_steps)
+    dq_h, dk_h, dv_h = dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+    rf.close()
+    rb.close()
     gq = w.q_global_rows()
     cu = w.cu
     allk = np.arange(w.total)
@@ -277,11 +384,9 @@ def _rank_fwd_bwd_sampled(w, label, active=None, two_calls=False):
     o_r, lse_r = A.forward(q64, k64, v64, gq[rows], allk, cu, w.scale)
     dq_ref, _, _ = A.backward(q64, k64, v64, do64, o_r, lse_r, gq[rows], allk, cu, w.scale,
                               cols=np.zeros(0, dtype=np.int64))
-    _check(f"dQ {label}", dq.cpu().numpy()[rows], dq_ref)
-    # (b) dK / dV of KV head 0 (its query heads) on keys sampled from every
-    #     non-empty step's chunks: the oracle forward on all rows of those heads
-    grp = w.hq // w.hkv
-    cols = set()
+    _check(f"dQ {label}", dq_h[rows], dq_ref)
+    # (b) dK / dV of every KV head at the sampled keys
+    cols = set(heavy)
     for st in [w.steps[i] for i in range(len(w.steps)) if two_calls or i in rb.active]:
         for a_, b_, _ in st.kv_segs:
             cols.update(rng.integers(a_, b_, size=6).tolist())
@@ -289,15 +394,24 @@ def _rank_fwd_bwd_sampled(w, label, active=None, two_calls=False):
     for s0 in cu[:-1].tolist():               # document starts (keys seen by the most rows)
         cols.add(s0)
     cols = np.array(sorted(cols))
-    qh, doh = f64(ql[:, :grp]), f64(dol[:, :grp])
-    kh, vh = k64[:, :1], v64[:, :1]
-    o_h, lse_h = A.forward(qh, kh, vh, gq, allk, cu, w.scale)
-    _, dk_ref, dv_ref = A.backward(qh, kh, vh, doh, o_h, lse_h, gq, allk, cu, w.scale,
+    say(f"  dK/dV sample: {len(cols)} keys x {w.hkv} KV heads (heaviest KV tile: {heavy_n} partner Q tiles, "
+        f"{len(heavy)} keys)")
+    grp = w.hq // w.hkv
+
+    def per_kv_head(g):
+        hs = slice(g * grp, (g + 1) * grp)
+        qh, doh = f64(ql[:, hs]), f64(dol[:, hs])
+        kh, vh = k64[:, g:g + 1], v64[:, g:g + 1]
+        o_h, lse_h = A.forward(qh, kh, vh, gq, allk, cu, w.scale)
+        _, dk_r, dv_r = A.backward(qh, kh, vh, doh, o_h, lse_h, gq, allk, cu, w.scale,
                                    rows=np.zeros(0, dtype=np.int64), cols=cols)
-    _check(f"dK {label} (KV head 0)", dk.cpu().numpy()[:, :1], dk_ref, cols)
-    _check(f"dV {label} (KV head 0)", dv.cpu().numpy()[:, :1], dv_ref, cols)
-    rf.close()
-    rb.close()
+        return dk_r[cols, 0], dv_r[cols, 0]
+
+    refs = par_map(per_kv_head, list(range(w.hkv)), label=f"{label} dK/dV")
+    dk_ref = np.stack([r[0] for r in refs], axis=1)
+    dv_ref = np.stack([r[1] for r in refs], axis=1)
+    _check(f"dK {label} (all KV heads)", dk_h[cols], dk_ref)
+    _check(f"dV {label} (all KV heads)", dv_h[cols], dv_ref)
 
 
 def test_zigzag_rank_fwd_bwd_sampled():
