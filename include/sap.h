@@ -342,6 +342,35 @@ sap_status sap_attn_bwd_dq(sap_plan_t plan, const void *q, const void *k, const 
                            int32_t hq, int32_t hkv, int32_t d, float scale,
                            float *dq, void *hip_stream);
 
+/*
+ * sap_attn_bwd_noalloc -- sap_attn_bwd for callers that cannot allocate
+ * device memory: code being captured into a HIP graph, tight serving or
+ * training loops, harnesses that forbid hipMalloc. It takes no workspace:
+ * the row terms and the split-tile partial sums go to a fixed device scratch
+ * array inside the library (SAP_BWD_NOALLOC_MAX_BYTES per GPU, reserved
+ * when the library is loaded and held until the process ends). The call
+ * allocates nothing -- no hipMalloc, hipFree or allocating library routine;
+ * its first call on a device looks the array's address up once
+ * (hipGetSymbolAddress) with that device current.
+ * Arguments, outputs and accumulation rules are those of sap_attn_bwd (same
+ * kernels, same bits). A plan whose sap_attn_bwd_workspace(plan, hq, hkv, d)
+ * exceeds SAP_BWD_NOALLOC_MAX_BYTES is refused with SAP_ERR_UNSUPPORTED
+ * before anything is launched (use sap_attn_bwd with a workspace); the 64 MiB
+ * cover e.g. a 64K-token five-head training shard (1.2 MiB) or a 512K-token
+ * four-head Ulysses shard (8 MiB), not a 32-head 128K zigzag rank (134 MiB).
+ * Every call on one GPU shares that GPU's scratch and it keeps the last
+ * call's contents: nothing needs clearing (each call writes every word it
+ * reads before reading it), but calls that overlap on one GPU -- on
+ * different streams, or from different threads -- race on it and must be
+ * serialised by the caller.
+ */
+#define SAP_BWD_NOALLOC_MAX_BYTES (64u << 20)
+sap_status sap_attn_bwd_noalloc(sap_plan_t plan, const void *q, const void *k, const void *v,
+                                const float *o, const float *lse_final, const void *dout,
+                                int64_t q_row_stride, int64_t kv_row_stride,
+                                int32_t hq, int32_t hkv, int32_t d, float scale,
+                                float *dq, float *dk, float *dv, void *hip_stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char *sap_last_error(void);
 

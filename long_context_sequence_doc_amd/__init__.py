@@ -21,12 +21,14 @@ __all__ = [
     "sap_plan", "sap_plan_upload", "sap_plan_info", "sap_plan_tiles", "sap_plan_q_tiles",
     "sap_plan_free", "sap_balance", "sap_attn_fwd", "sap_attn_fwd_merge", "sap_lse_merge", "sap_attn_bwd_workspace", "sap_attn_bwd",
     "sap_attn_bwd_rowterm", "sap_attn_bwd_accumulate", "sap_attn_bwd_dkdv", "sap_attn_bwd_dq",
+    "sap_attn_bwd_noalloc", "SAP_BWD_NOALLOC_MAX_BYTES",
     "sap_last_error", "sap_version", "lib_path", "SAP_TILE_FULL", "SAP_TILE_DIAGONAL",
     "SAP_TILE_PARTIAL",
 ]
 
 SAP_OK, SAP_ERR_INVALID_ARG, SAP_ERR_UNSUPPORTED, SAP_ERR_NO_MEMORY, SAP_ERR_HIP, SAP_ERR_STATE = range(6)
 SAP_TILE_FULL, SAP_TILE_DIAGONAL, SAP_TILE_PARTIAL = 0, 1, 2
+SAP_BWD_NOALLOC_MAX_BYTES = 64 << 20   # the fixed scratch of sap_attn_bwd_noalloc (include/sap.h)
 _STATUS = {0: "SAP_OK", 1: "SAP_ERR_INVALID_ARG", 2: "SAP_ERR_UNSUPPORTED", 3: "SAP_ERR_NO_MEMORY",
            4: "SAP_ERR_HIP", 5: "SAP_ERR_STATE"}
 
@@ -87,6 +89,8 @@ _sigs = {
     "sap_attn_bwd_dkdv": ([_P, _P, _P, _P, _P, _P, _P, _i64, _i64, _i32, _i32, _i32, _f32, _P, _P, _P, _sz, _P],
                           _i32),
     "sap_attn_bwd_dq": ([_P, _P, _P, _P, _P, _P, _P, _i64, _i64, _i32, _i32, _i32, _f32, _P, _P], _i32),
+    "sap_attn_bwd_noalloc": ([_P, _P, _P, _P, _P, _P, _P, _i64, _i64, _i32, _i32, _i32, _f32, _P, _P, _P, _P],
+                             _i32),
     "sap_last_error": ([], ctypes.c_char_p),
     "sap_version": ([], _i32),
 }
@@ -264,3 +268,10 @@ def sap_attn_bwd_dq(plan: Plan, q, k, v, lse_final, delta, dout, q_row_stride: i
                     hkv: int, d: int, scale: float, dq, stream=None):
     _check(_lib.sap_attn_bwd_dq(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(lse_final), _ptr(delta), _ptr(dout),
                                 q_row_stride, kv_row_stride, hq, hkv, d, scale, _ptr(dq), _stream(stream)))
+
+
+def sap_attn_bwd_noalloc(plan: Plan, q, k, v, o, lse_final, dout, q_row_stride: int, kv_row_stride: int, hq: int,
+                         hkv: int, d: int, scale: float, dq, dk, dv, stream=None):
+    _check(_lib.sap_attn_bwd_noalloc(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_final), _ptr(dout),
+                                     q_row_stride, kv_row_stride, hq, hkv, d, scale, _ptr(dq), _ptr(dk), _ptr(dv),
+                                     _stream(stream)))

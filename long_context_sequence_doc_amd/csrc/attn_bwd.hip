@@ -44,9 +44,18 @@
 #include <climits>
 #include <cstdint>
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "kernels.h"
+
+// Device scratch of the allocation-free backward (sap_attn_bwd_noalloc): the
+// row terms and split-tile partial sums that sap_attn_bwd keeps in the
+// caller's workspace. One copy per GPU, held until the process ends. Host
+// code never passes this name to a kernel (on the host it is only a stand-in
+// for the symbol): its device address comes from hipGetSymbolAddress, once
+// per device (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[sap::kNoAllocScratchBytes];
 
 namespace sap {
 namespace {
@@ -868,6 +877,27 @@ const char *attn_bwd_limits(const BwdLaunch &a) {
   if (int64_t(a.n_reduce) * a.hkv * NT > cap) return "split-tile reduce grid too large";
   if (dq_blocks(a) * 128 * dq_heads(a.hq / a.hkv) > cap) return "dQ grid too large (Q tiles x query heads)";
   return nullptr;
+}
+
+hipError_t noalloc_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    // with this device current: its own copy of the array, at its own address
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_bwd_rowterm(const BwdLaunch &a, hipStream_t stream) {

@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <cstdint>
 
 #include "sap_internal.h"
@@ -77,5 +78,11 @@ hipError_t launch_attn_bwd_dkdv(const BwdLaunch &a, hipStream_t stream);
 // dq given a.delta: the Q-major kernel
 hipError_t launch_attn_bwd_dq(const BwdLaunch &a, hipStream_t stream);
 const char *attn_bwd_limits(const BwdLaunch &a);
+
+// Bytes of the allocation-free backward's device scratch (one per GPU).
+constexpr size_t kNoAllocScratchBytes = size_t(SAP_BWD_NOALLOC_MAX_BYTES);
+// Device address of that scratch on the current device (looked up once per
+// device with hipGetSymbolAddress, then cached). Allocates nothing.
+hipError_t noalloc_scratch(void **ptr);
 
 }  // namespace sap

@@ -469,7 +469,11 @@ sap_status sap_attn_bwd_dq(sap_plan_t plan, const void *q, const void *k, const 
                           nullptr, nullptr, nullptr, 0, kDq, hip_stream);
 }
 
-sap_status sap_attn_bwd(sap_plan_t plan, const void *q, const void *k, const void *v, const float *o,
+}  // extern "C"
+
+namespace {
+
+sap_status bwd_impl(sap_plan_t plan, const void *q, const void *k, const void *v, const float *o,
                         const float *lse_final, const void *dout, int64_t q_row_stride,
                         int64_t kv_row_stride, int32_t hq, int32_t hkv, int32_t d, float scale,
                         float *dq, float *dk, float *dv, void *workspace, size_t workspace_bytes,
@@ -495,6 +499,44 @@ sap_status sap_attn_bwd(sap_plan_t plan, const void *q, const void *k, const voi
   if (e != hipSuccess) return hip_fail(e, "bwd row-term launch");
   if ((s = accumulate_launch(ba, kBoth, stream)) != SAP_OK) return s;
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+sap_status sap_attn_bwd(sap_plan_t plan, const void *q, const void *k, const void *v, const float *o,
+                        const float *lse_final, const void *dout, int64_t q_row_stride,
+                        int64_t kv_row_stride, int32_t hq, int32_t hkv, int32_t d, float scale,
+                        float *dq, float *dk, float *dv, void *workspace, size_t workspace_bytes,
+                        void *hip_stream) {
+  return bwd_impl(plan, q, k, v, o, lse_final, dout, q_row_stride, kv_row_stride, hq, hkv, d, scale, dq, dk, dv,
+                  workspace, workspace_bytes, hip_stream);
+}
+
+sap_status sap_attn_bwd_noalloc(sap_plan_t plan, const void *q, const void *k, const void *v, const float *o,
+                                const float *lse_final, const void *dout, int64_t q_row_stride,
+                                int64_t kv_row_stride, int32_t hq, int32_t hkv, int32_t d, float scale,
+                                float *dq, float *dk, float *dv, void *hip_stream) {
+  sap_status s = check_bwd_common(plan, hq, hkv, d);
+  if (s != SAP_OK) return s;
+  const size_t need = sap_attn_bwd_workspace(plan, hq, hkv, d);
+  if (need > sap::kNoAllocScratchBytes)
+    return fail(SAP_ERR_UNSUPPORTED, "sap_attn_bwd_noalloc: the plan needs " + std::to_string(need) +
+                                         " bytes of scratch, more than its fixed " +
+                                         std::to_string(sap::kNoAllocScratchBytes) +
+                                         " (use sap_attn_bwd with a workspace)");
+  if (plan->p.kv_work.empty()) {
+    if (!(scale > 0.f) || !(scale < 1e30f)) return fail(SAP_ERR_INVALID_ARG, "scale must be positive and finite");
+    return ok();
+  }
+  // host checks first: nothing touches a device for a call that is refused
+  if ((s = check_uploaded(plan)) != SAP_OK) return s;
+  void *ws = nullptr;
+  const hipError_t e = sap::noalloc_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the backward scratch");
+  return bwd_impl(plan, q, k, v, o, lse_final, dout, q_row_stride, kv_row_stride, hq, hkv, d, scale, dq, dk, dv, ws,
+                  sap::kNoAllocScratchBytes, hip_stream);
 }
 
 }  // extern "C"

@@ -165,3 +165,20 @@ def test_backward_halves_validate_before_launch():
     with pytest.raises(sap.SapError) as e:
         sap.sap_attn_bwd_dq(pb, 16, 16, 16, 16, 16, 16, 128, 128, 2, 2, 64, 0.1, 16, stream=0)
     assert e.value.status == sap.SAP_ERR_STATE
+
+
+def test_noalloc_backward_refuses_plans_beyond_its_scratch_on_the_host():
+    """sap_attn_bwd_noalloc checks the plan's scratch need against its fixed
+    SAP_BWD_NOALLOC_MAX_BYTES before it touches a device: a plan that needs
+    more is refused with SAP_ERR_UNSUPPORTED (here never uploaded, so nothing
+    could reach a GPU)."""
+    plan = sap.sap_plan([0, 8192], [(4096, 8192, 0)], [(0, 4096, 0)], 64, 128)
+    assert sap.sap_attn_bwd_workspace(plan, 32, 16, 128) > sap.SAP_BWD_NOALLOC_MAX_BYTES
+    with pytest.raises(sap.SapError) as e:
+        sap.sap_attn_bwd_noalloc(plan, 16, 16, 16, 16, 16, 16, 32 * 128, 16 * 128, 32, 16, 128, 0.088, 16, 16, 16,
+                                 stream=0)
+    assert e.value.status == sap.SAP_ERR_UNSUPPORTED and "scratch" in str(e.value)
+    # within the limit, the call goes on to the plan checks (not uploaded)
+    with pytest.raises(sap.SapError) as e:
+        sap.sap_attn_bwd_noalloc(plan, 16, 16, 16, 16, 16, 16, 2 * 128, 128, 2, 1, 128, 0.088, 16, 16, 16, stream=0)
+    assert e.value.status == sap.SAP_ERR_STATE
