@@ -155,3 +155,61 @@ def oracle_forward_rows(q, k, v, gq, gk, cu, scale, rows, label="", piece=256):
         hq, d = q.shape[1], q.shape[2]
         return np.zeros((0, hq, d)), np.zeros((hq, 0))
     return np.concatenate([r[0] for r in res], axis=0), np.concatenate([r[1] for r in res], axis=1)
+
+
+def oracle_fwd_bwd_full(q, k, v, do, gq, cu, scale, label="", max_rows=1024):
+    """The oracle's forward and backward of a rank at full size, every row:
+    q, do local rows [Tq, Hq, D], k, v whole-sequence [T, Hkv, D] (bf16 bit
+    patterns or floats), gq the global position of every local row. The
+    forward runs in pieces of rows; the backward in (KV head, document, block
+    of <= max_rows query rows) pieces, which is exact: a dQ row is a sum over
+    its own document's keys, and a key's dK / dV is the sum of the pieces'
+    partial sums over that document's rows (added here in a fixed order).
+    Returns O, LSE, dQ, dK, dV in float64."""
+    from oracle import attention as A
+    conv = lambda x: f64(x) if x.dtype == np.uint16 else np.asarray(x, dtype=np.float64)
+    gq = np.asarray(gq, dtype=np.int64)
+    cu = np.asarray(cu, dtype=np.int64)
+    tq, hq = q.shape[0], q.shape[1]
+    total, hkv, d = k.shape
+    grp = hq // hkv
+    k64, v64 = conv(k), conv(v)
+    o, lse = oracle_forward_rows(q, k64, v64, gq, np.arange(total), cu, scale, np.arange(tq), label=f"{label} fwd")
+    doc_q = np.searchsorted(cu, gq, side="right") - 1
+    pieces = []
+    for g in range(hkv):
+        for dd in np.unique(doc_q):
+            rows = np.nonzero(doc_q == dd)[0]
+            for i in range(0, len(rows), max_rows):
+                pieces.append((g, int(dd), rows[i:i + max_rows]))
+
+    def one(piece):
+        g, dd, rows = piece
+        hs = slice(g * grp, (g + 1) * grp)
+        keys = np.arange(cu[dd], cu[dd + 1])
+        return A.backward(conv(q[rows][:, hs]), k64[keys, g:g + 1], v64[keys, g:g + 1], conv(do[rows][:, hs]),
+                          o[rows][:, hs], lse[hs][:, rows], gq[rows], keys, cu, scale)
+
+    res = par_map(one, pieces, label=f"{label} bwd")
+    dq = np.zeros((tq, hq, d))
+    dk = np.zeros((total, hkv, d))
+    dv = np.zeros((total, hkv, d))
+    for (g, dd, rows), (pq, pk, pv) in zip(pieces, res):
+        hs = slice(g * grp, (g + 1) * grp)
+        keys = slice(int(cu[dd]), int(cu[dd + 1]))
+        dq[rows, hs] = pq
+        dk[keys, g:g + 1] += pk
+        dv[keys, g:g + 1] += pv
+    return o, lse, dq, dk, dv
+
+
+@functools.lru_cache(maxsize=2)
+def full_reference(name: str):
+    """The oracle's O, LSE, dQ, dK, dV of a named workload's rank on every row
+    and key (computed once per test process and shared by the tests of its
+    different schedules, which must all reproduce it)."""
+    w = W.by_name(name)
+    t = tensors(name, True)
+    say(f"  oracle reference of {w.name}: every row and key, forward and backward")
+    ql, dol = W.local_rows(t.q, w.q_segs), W.local_rows(t.do, w.q_segs)
+    return oracle_fwd_bwd_full(ql, t.k, t.v, dol, w.q_global_rows(), w.cu, w.scale, label=w.name)

@@ -12,7 +12,7 @@ import pytest
 
 import workloads as W
 from oracle import attention as A
-from tests.gpu_common import TOL_O, f64, need_gpu, par_map, say, tensors, to_dev
+from tests.gpu_common import TOL_O, f64, full_reference, need_gpu, par_map, say, tensors, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -264,15 +264,16 @@ def test_ring_steps_accumulate_to_full_gradient():
     _check("dV one call", dv.cpu().numpy(), dv_ref)
 
 
-def test_training_fwd_bwd_sampled():
+def test_training_fwd_bwd_all_rows():
     """64K training sequence (5 heads, 30 documents incl. 1-token ones):
-    GPU forward then GPU backward; sampled dQ rows and dK/dV rows vs the oracle."""
+    GPU forward then GPU backward; every dQ row and every dK / dV key against
+    the oracle (which runs its own forward for the final O / LSE)."""
     sap = _sap()
     import torch
     from long_context_sequence_doc_amd.rank import RankForward
     w = W.training()
     t = tensors("train", True)
-    say("case train_64k_5heads fwd+bwd, sampled rows")
+    say("case train_64k_5heads fwd+bwd, every row and key")
     rf = RankForward(w.cu, w.q_segs, [s.kv_segs for s in w.steps], w.hq, w.hkv, w.d, w.scale)
     qd, kd, vd, dod = to_dev(t.q), to_dev(t.k), to_dev(t.v), to_dev(t.do)
     o, lse = rf.run(qd, kd, vd, qd.stride(0), kd.stride(0))
@@ -283,35 +284,12 @@ def test_training_fwd_bwd_sampled():
                      w.scale, dq, dk, dv)
     torch.cuda.synchronize()
     del keep
-    g = np.arange(w.total)
-    rng = np.random.default_rng(5)
-    cu = w.cu
-    # dQ rows: seeded random rows, document starts (1-token documents included), the end
-    pick = set(rng.integers(0, w.total, size=96).tolist())
-    for s0 in cu[:-1].tolist():
-        pick.update((s0, min(w.total - 1, s0 + 1)))
-    pick.update(range(w.total - 8, w.total))
-    rows = np.array(sorted(pick))
-    # dK/dV rows: the last 3 keys of every document (seen by a few queries
-    # only), every document's first two keys (seen by every query of the
-    # document, through its long unmasked partner lists) and seeded keys
-    cols = {c for e in cu[1:].tolist() for c in range(max(0, e - 3), e)}
-    cols.update(c for s0 in cu[:-1].tolist() for c in (s0, s0 + 1) if c < w.total)
-    cols.update(rng.integers(0, w.total, size=64).tolist())
-    cols = np.array(sorted(cols))
-    # the oracle's own forward, on every query row those gradients depend on
-    need = set(rows.tolist())
-    for c in cols.tolist():
-        e = int(cu[np.searchsorted(cu, c, side="right")])
-        need.update(range(c, e))
-    need = np.array(sorted(need))
-    o_ref, lse_ref = A.forward(f64(t.q), f64(t.k), f64(t.v), g, g, cu, w.scale, rows=need)
-    dq_ref, dk_ref, dv_ref = A.backward(f64(t.q), f64(t.k), f64(t.v), f64(t.do), o_ref, lse_ref, g, g, cu,
-                                        w.scale, rows=rows, cols=cols)
-    _check("dQ train", dq.cpu().numpy(), dq_ref, rows)
-    _check("dK train", dk.cpu().numpy(), dk_ref, cols)
-    _check("dV train", dv.cpu().numpy(), dv_ref, cols)
+    dq_h, dk_h, dv_h = dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
     rf.close()
+    _, _, dq_ref, dk_ref, dv_ref = full_reference("train")
+    _check("dQ train (all rows)", dq_h, dq_ref)
+    _check("dK train (all keys)", dk_h, dk_ref)
+    _check("dV train (all keys)", dv_h, dv_ref)
 
 
 def _heaviest_kv_tile_keys(rb, step_kv_segs):
@@ -414,19 +392,59 @@ def _rank_fwd_bwd_sampled(w, label, active=None, two_calls=False):
     _check(f"dV {label} (all KV heads)", dv_h[cols], dv_ref)
 
 
-def test_zigzag_rank_fwd_bwd_sampled():
+def _zigzag_fwd_bwd_all_rows(label, two_calls):
+    """128K zigzag GQA rank 3: forward with merges, row terms once, backward
+    per non-empty step (or as own + remote calls); every dQ row and every
+    dK / dV key of every head against the oracle's full reference; also every
+    key of the backward plans' heaviest (split) KV tile is among them."""
+    import torch
+    from long_context_sequence_doc_amd.rank import RankBackward, RankForward
+    w = W.zigzag_rank(3)
+    t = tensors("zigzag", True)
+    steps = [s.kv_segs for s in w.steps]
+    if two_calls:
+        rf = RankForward.local_then_remote(w.cu, w.q_segs, steps, w.hq, w.hkv, w.d, w.scale)
+        rb = RankBackward.local_then_remote(w.cu, w.q_segs, steps, w.hq, w.hkv, w.d, w.scale)
+        bwd_steps = [steps[0], [seg for segs in steps[1:] for seg in segs]]
+        assert rb.active == [0, 1]
+    else:
+        rf = RankForward(w.cu, w.q_segs, steps, w.hq, w.hkv, w.d, w.scale)
+        rb = RankBackward(w.cu, w.q_segs, steps, w.hq, w.hkv, w.d, w.scale)
+        bwd_steps = steps
+        assert rb.active == [0, 1, 7]
+    ql, dol = W.local_rows(t.q, w.q_segs), W.local_rows(t.do, w.q_segs)
+    qd, dod, kd, vd = to_dev(ql), to_dev(dol), to_dev(t.k), to_dev(t.v)
+    o, lse = rf.run(qd, kd, vd, qd.stride(0), kd.stride(0))
+    dq = torch.zeros((w.tq, w.hq, w.d), device="cuda")
+    dk = torch.zeros((w.total, w.hkv, w.d), device="cuda")
+    dv = torch.zeros_like(dk)
+    rb.run(qd, kd, vd, o, lse, dod, qd.stride(0), kd.stride(0), dq, dk, dv)
+    torch.cuda.synchronize()
+    heavy_n, heavy = _heaviest_kv_tile_keys(rb, bwd_steps)
+    say(f"  heaviest KV tile of the backward plans: {heavy_n} partner Q tiles (split), keys {heavy[0]}..{heavy[-1]}")
+    dq_h, dk_h, dv_h = dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+    rf.close()
+    rb.close()
+    _, _, dq_ref, dk_ref, dv_ref = full_reference("zigzag")
+    _check(f"dQ {label} (all rows)", dq_h, dq_ref)
+    _check(f"dK {label} (all keys)", dk_h, dk_ref)
+    _check(f"dV {label} (all keys)", dv_h, dv_ref)
+    _check(f"dK {label} (heaviest split KV tile)", dk_h[heavy], dk_ref[heavy])
+
+
+def test_zigzag_rank_fwd_bwd_all_rows():
     """The benchmarked configuration: 128K zigzag GQA rank 3 (ring steps 0, 1, 7)."""
     _sap()
-    say("case zigzag_sp8_128k_gqa_rank3 fwd+bwd (ring steps), sampled rows")
-    _rank_fwd_bwd_sampled(W.zigzag_rank(3), "zigzag", active=[0, 1, 7])
+    say("case zigzag_sp8_128k_gqa_rank3 fwd+bwd (ring steps), every row and key")
+    _zigzag_fwd_bwd_all_rows("zigzag", two_calls=False)
 
 
-def test_zigzag_rank_two_calls_sampled():
+def test_zigzag_rank_two_calls_all_rows():
     """128K zigzag GQA rank 3, forward and backward as two calls each (own
     chunks, then all remote chunks at once)."""
     _sap()
-    say("case zigzag_sp8_128k_gqa_rank3 fwd+bwd as local + remote calls, sampled rows")
-    _rank_fwd_bwd_sampled(W.zigzag_rank(3), "zigzag two calls", active=[0, 1], two_calls=True)
+    say("case zigzag_sp8_128k_gqa_rank3 fwd+bwd as local + remote calls, every row and key")
+    _zigzag_fwd_bwd_all_rows("zigzag two calls", two_calls=True)
 
 
 def test_balanced_rank_fwd_bwd_sampled():

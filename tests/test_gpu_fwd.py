@@ -9,8 +9,8 @@ import pytest
 
 import workloads as W
 from oracle import attention as A
-from tests.gpu_common import (TOL_LSE, TOL_O, compare, f64, need_gpu, oracle_forward_rows, sample_rows, say,
-                               tensors, to_dev, ulysses_rows)
+from tests.gpu_common import (TOL_LSE, TOL_O, compare, f64, full_reference, need_gpu, oracle_forward_rows,
+                               sample_rows, say, tensors, to_dev, ulysses_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -336,28 +336,26 @@ def test_fused_merge_random(seed, block_m):
     sap.sap_plan_free(pb)
 
 
-def test_zigzag_gqa_headline_sampled():
+def test_zigzag_gqa_headline_all_rows():
     """128K zigzag GQA shard (rank 3), the benchmarked configuration (merges
-    folded into the forward); sampled rows."""
+    folded into the forward): every row and head against the oracle."""
     _sap()
-    say("case zigzag_sp8_128k_gqa_rank3: 3 non-empty steps, fused merges, sampled rows")
+    say("case zigzag_sp8_128k_gqa_rank3: 3 non-empty steps, fused merges, every row")
     w, t, rf, q, k, v = _rank_run("zigzag")
     assert rf.active == [0, 1, 7]
-    gq = w.q_global_rows()
-    rows = sample_rows(gq, w.cu)
-    ro, rl = A.forward(f64(W.local_rows(t.q, w.q_segs)), f64(t.k), f64(t.v), gq, np.arange(w.total), w.cu, w.scale,
-                       rows=rows)
-    compare(rf.o.cpu().numpy(), rf.lse.cpu().numpy(), ro, rl, rows=rows, label="zigzag merged")
+    o, lse = rf.o.cpu().numpy(), rf.lse.cpu().numpy()
     rf.close()
+    ro, rl, _, _, _ = full_reference("zigzag")
+    compare(o, lse, ro, rl, label="zigzag merged (all rows)")
 
 
-def test_zigzag_single_call_sampled():
+def test_zigzag_single_call_all_rows():
     """128K zigzag GQA shard (rank 3) as one launch over all non-empty steps'
-    KV (concatenated plan, no merges): sampled rows against the oracle."""
+    KV (concatenated plan, no merges): every row and head."""
     _sap()
     import torch
     from long_context_sequence_doc_amd.rank import RankForward
-    say("case zigzag_sp8_128k_gqa_rank3: one call over all steps' KV, sampled rows")
+    say("case zigzag_sp8_128k_gqa_rank3: one call over all steps' KV, every row")
     w = W.by_name("zigzag")
     t = tensors("zigzag")
     rc = RankForward.concatenated(w.cu, w.q_segs, [s.kv_segs for s in w.steps], w.hq, w.hkv, w.d, w.scale)
@@ -366,12 +364,10 @@ def test_zigzag_single_call_sampled():
     k, v = to_dev(t.k), to_dev(t.v)
     rc.run(q, k, v, q.stride(0), k.stride(0))
     torch.cuda.synchronize()
-    gq = w.q_global_rows()
-    rows = sample_rows(gq, w.cu)
-    ro, rl = A.forward(f64(W.local_rows(t.q, w.q_segs)), f64(t.k), f64(t.v), gq, np.arange(w.total), w.cu, w.scale,
-                       rows=rows)
-    compare(rc.o.cpu().numpy(), rc.lse.cpu().numpy(), ro, rl, rows=rows, label="zigzag single call")
+    o, lse = rc.o.cpu().numpy(), rc.lse.cpu().numpy()
     rc.close()
+    ro, rl, _, _, _ = full_reference("zigzag")
+    compare(o, lse, ro, rl, label="zigzag single call (all rows)")
 
 
 def test_balanced_rank_sampled():
@@ -401,38 +397,35 @@ def test_balanced_rank_sampled():
     rf.close()
 
 
-def test_zigzag_local_then_remote_sampled():
+def test_zigzag_local_then_remote_all_rows():
     """128K zigzag GQA rank 3 as two calls: its own chunks, then every remote
-    chunk together with the merge in the epilogue; sampled rows."""
+    chunk together with the merge in the epilogue; every row and head."""
     _sap()
     import torch
     from long_context_sequence_doc_amd.rank import RankForward
     w = W.zigzag_rank(3)
     t = tensors("zigzag")
-    say("case zigzag_sp8_128k_gqa_rank3: local step + one merged call over all remote chunks, sampled rows")
+    say("case zigzag_sp8_128k_gqa_rank3: local step + one merged call over all remote chunks, every row")
     rf = RankForward.local_then_remote(w.cu, w.q_segs, [s.kv_segs for s in w.steps], w.hq, w.hkv, w.d, w.scale)
     assert rf.active == [0, 1]
     q = to_dev(W.local_rows(t.q, w.q_segs))
     k, v = to_dev(t.k), to_dev(t.v)
     rf.run(q, k, v, q.stride(0), k.stride(0))
     torch.cuda.synchronize()
-    gq = w.q_global_rows()
-    rows = sample_rows(gq, w.cu)
-    ro, rl = A.forward(f64(W.local_rows(t.q, w.q_segs)), f64(t.k), f64(t.v), gq, np.arange(w.total), w.cu, w.scale,
-                       rows=rows)
-    compare(rf.o.cpu().numpy(), rf.lse.cpu().numpy(), ro, rl, rows=rows, label="zigzag local + remote")
+    o, lse = rf.o.cpu().numpy(), rf.lse.cpu().numpy()
     rf.close()
+    ro, rl, _, _, _ = full_reference("zigzag")
+    compare(o, lse, ro, rl, label="zigzag local + remote (all rows)")
 
 
-def test_training_forward_sampled():
+def test_training_forward_all_rows():
     _sap()
-    say("case train_64k_5heads forward, sampled rows")
+    say("case train_64k_5heads forward, every row")
     w, t, rf, q, k, v = _rank_run("train")
-    g = np.arange(w.total)
-    rows = sample_rows(g, w.cu, n_random=512)
-    ro, rl = A.forward(f64(t.q), f64(t.k), f64(t.v), g, g, w.cu, w.scale, rows=rows)
-    compare(rf.o.cpu().numpy(), rf.lse.cpu().numpy(), ro, rl, rows=rows, label="train fwd")
+    o, lse = rf.o.cpu().numpy(), rf.lse.cpu().numpy()
     rf.close()
+    ro, rl, _, _, _ = full_reference("train")
+    compare(o, lse, ro, rl, label="train fwd (all rows)")
 
 
 @pytest.mark.parametrize("name", ["ulysses", "ulysses_gqa"])
