@@ -203,13 +203,23 @@ def oracle_fwd_bwd_full(q, k, v, do, gq, cu, scale, label="", max_rows=1024):
     return o, lse, dq, dk, dv
 
 
-@functools.lru_cache(maxsize=2)
+def balanced_rank3():
+    """Rank 3 of the 128K sequence in the document-aware balanced layout
+    (1024-row chunks), the chunk owners taken from the oracle's assignment."""
+    from oracle import balance as B
+    z = W.zigzag_rank(3)
+    owner = B.balance(z.cu, 8, 1024)[0]
+    return W.owner_rank(z, list(owner), 3, 1024, "balanced")
+
+
+@functools.lru_cache(maxsize=3)
 def full_reference(name: str):
     """The oracle's O, LSE, dQ, dK, dV of a named workload's rank on every row
     and key (computed once per test process and shared by the tests of its
-    different schedules, which must all reproduce it)."""
-    w = W.by_name(name)
-    t = tensors(name, True)
+    different schedules, which must all reproduce it). ``balanced`` is rank 3
+    of the 128K sequence in the balanced layout (inputs of ``zigzag``)."""
+    w = balanced_rank3() if name == "balanced" else W.by_name(name)
+    t = tensors("zigzag" if name == "balanced" else name, True)
     say(f"  oracle reference of {w.name}: every row and key, forward and backward")
     ql, dol = W.local_rows(t.q, w.q_segs), W.local_rows(t.do, w.q_segs)
     return oracle_fwd_bwd_full(ql, t.k, t.v, dol, w.q_global_rows(), w.cu, w.scale, label=w.name)

@@ -12,7 +12,7 @@ import pytest
 
 import workloads as W
 from oracle import attention as A
-from tests.gpu_common import TOL_O, f64, full_reference, need_gpu, par_map, say, tensors, to_dev
+from tests.gpu_common import TOL_O, f64, full_reference, need_gpu, say, tensors, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -312,13 +312,11 @@ def _heaviest_kv_tile_keys(rb, step_kv_segs):
     return best, keys
 
 
-def _rank_fwd_bwd_sampled(w, label, active=None, two_calls=False):
-    """Forward over the ring steps with merges, row terms once, backward per
-    non-empty step. dQ on sampled rows (all heads); dK / dV on all KV heads
-    at sampled keys: seeded keys of every non-empty step's chunks, each
-    chunk's ends, every document start (the keys the most queries see) and
-    every key of the backward plans' heaviest KV tile (split into chunks).
-    The oracle runs its own forward for the final O / LSE."""
+def _rank_fwd_bwd_all_rows(w, ref, label, active, two_calls=False):
+    """A 128K-sequence rank: forward with merges, row terms once, backward per
+    non-empty step (or as own + remote calls); every dQ row and every dK / dV
+    key of every head against the oracle's full reference ``ref``; the keys
+    of the backward plans' heaviest (split) KV tile are reported on their own."""
     import torch
     from long_context_sequence_doc_amd.rank import RankBackward, RankForward
     t = tensors("zigzag", True)
@@ -342,90 +340,11 @@ def _rank_fwd_bwd_sampled(w, label, active=None, two_calls=False):
     rb.run(qd, kd, vd, o, lse, dod, qd.stride(0), kd.stride(0), dq, dk, dv)
     torch.cuda.synchronize()
     heavy_n, heavy = _heaviest_kv_tile_keys(rb, bwd_steps)
-    dq_h, dk_h, dv_h = dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
-    rf.close()
-    rb.close()
-    gq = w.q_global_rows()
-    cu = w.cu
-    allk = np.arange(w.total)
-    k64, v64 = f64(t.k), f64(t.v)
-    # (a) dQ on sampled rows, all heads: the oracle forward on those rows only
-    rng = np.random.default_rng(5)
-    rows = set(rng.integers(0, w.tq, size=48).tolist())
-    pos = {g: r for r, g in enumerate(gq.tolist())}
-    for s0 in cu[:-1].tolist():
-        for g in (s0, s0 + 1):
-            if g in pos:
-                rows.add(pos[g])
-    rows = np.array(sorted(rows))
-    q64, do64 = f64(ql[rows]), f64(dol[rows])
-    o_r, lse_r = A.forward(q64, k64, v64, gq[rows], allk, cu, w.scale)
-    dq_ref, _, _ = A.backward(q64, k64, v64, do64, o_r, lse_r, gq[rows], allk, cu, w.scale,
-                              cols=np.zeros(0, dtype=np.int64))
-    _check(f"dQ {label}", dq_h[rows], dq_ref)
-    # (b) dK / dV of every KV head at the sampled keys
-    cols = set(heavy)
-    for st in [w.steps[i] for i in range(len(w.steps)) if two_calls or i in rb.active]:
-        for a_, b_, _ in st.kv_segs:
-            cols.update(rng.integers(a_, b_, size=6).tolist())
-            cols.update((a_, b_ - 1))
-    for s0 in cu[:-1].tolist():               # document starts (keys seen by the most rows)
-        cols.add(s0)
-    cols = np.array(sorted(cols))
-    say(f"  dK/dV sample: {len(cols)} keys x {w.hkv} KV heads (heaviest KV tile: {heavy_n} partner Q tiles, "
-        f"{len(heavy)} keys)")
-    grp = w.hq // w.hkv
-
-    def per_kv_head(g):
-        hs = slice(g * grp, (g + 1) * grp)
-        qh, doh = f64(ql[:, hs]), f64(dol[:, hs])
-        kh, vh = k64[:, g:g + 1], v64[:, g:g + 1]
-        o_h, lse_h = A.forward(qh, kh, vh, gq, allk, cu, w.scale)
-        _, dk_r, dv_r = A.backward(qh, kh, vh, doh, o_h, lse_h, gq, allk, cu, w.scale,
-                                   rows=np.zeros(0, dtype=np.int64), cols=cols)
-        return dk_r[cols, 0], dv_r[cols, 0]
-
-    refs = par_map(per_kv_head, list(range(w.hkv)), label=f"{label} dK/dV")
-    dk_ref = np.stack([r[0] for r in refs], axis=1)
-    dv_ref = np.stack([r[1] for r in refs], axis=1)
-    _check(f"dK {label} (all KV heads)", dk_h[cols], dk_ref)
-    _check(f"dV {label} (all KV heads)", dv_h[cols], dv_ref)
-
-
-def _zigzag_fwd_bwd_all_rows(label, two_calls):
-    """128K zigzag GQA rank 3: forward with merges, row terms once, backward
-    per non-empty step (or as own + remote calls); every dQ row and every
-    dK / dV key of every head against the oracle's full reference; also every
-    key of the backward plans' heaviest (split) KV tile is among them."""
-    import torch
-    from long_context_sequence_doc_amd.rank import RankBackward, RankForward
-    w = W.zigzag_rank(3)
-    t = tensors("zigzag", True)
-    steps = [s.kv_segs for s in w.steps]
-    if two_calls:
-        rf = RankForward.local_then_remote(w.cu, w.q_segs, steps, w.hq, w.hkv, w.d, w.scale)
-        rb = RankBackward.local_then_remote(w.cu, w.q_segs, steps, w.hq, w.hkv, w.d, w.scale)
-        bwd_steps = [steps[0], [seg for segs in steps[1:] for seg in segs]]
-        assert rb.active == [0, 1]
-    else:
-        rf = RankForward(w.cu, w.q_segs, steps, w.hq, w.hkv, w.d, w.scale)
-        rb = RankBackward(w.cu, w.q_segs, steps, w.hq, w.hkv, w.d, w.scale)
-        bwd_steps = steps
-        assert rb.active == [0, 1, 7]
-    ql, dol = W.local_rows(t.q, w.q_segs), W.local_rows(t.do, w.q_segs)
-    qd, dod, kd, vd = to_dev(ql), to_dev(dol), to_dev(t.k), to_dev(t.v)
-    o, lse = rf.run(qd, kd, vd, qd.stride(0), kd.stride(0))
-    dq = torch.zeros((w.tq, w.hq, w.d), device="cuda")
-    dk = torch.zeros((w.total, w.hkv, w.d), device="cuda")
-    dv = torch.zeros_like(dk)
-    rb.run(qd, kd, vd, o, lse, dod, qd.stride(0), kd.stride(0), dq, dk, dv)
-    torch.cuda.synchronize()
-    heavy_n, heavy = _heaviest_kv_tile_keys(rb, bwd_steps)
     say(f"  heaviest KV tile of the backward plans: {heavy_n} partner Q tiles (split), keys {heavy[0]}..{heavy[-1]}")
     dq_h, dk_h, dv_h = dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
     rf.close()
     rb.close()
-    _, _, dq_ref, dk_ref, dv_ref = full_reference("zigzag")
+    _, _, dq_ref, dk_ref, dv_ref = full_reference(ref)
     _check(f"dQ {label} (all rows)", dq_h, dq_ref)
     _check(f"dK {label} (all keys)", dk_h, dk_ref)
     _check(f"dV {label} (all keys)", dv_h, dv_ref)
@@ -436,7 +355,7 @@ def test_zigzag_rank_fwd_bwd_all_rows():
     """The benchmarked configuration: 128K zigzag GQA rank 3 (ring steps 0, 1, 7)."""
     _sap()
     say("case zigzag_sp8_128k_gqa_rank3 fwd+bwd (ring steps), every row and key")
-    _zigzag_fwd_bwd_all_rows("zigzag", two_calls=False)
+    _rank_fwd_bwd_all_rows(W.zigzag_rank(3), "zigzag", "zigzag", active=[0, 1, 7])
 
 
 def test_zigzag_rank_two_calls_all_rows():
@@ -444,20 +363,21 @@ def test_zigzag_rank_two_calls_all_rows():
     chunks, then all remote chunks at once)."""
     _sap()
     say("case zigzag_sp8_128k_gqa_rank3 fwd+bwd as local + remote calls, every row and key")
-    _zigzag_fwd_bwd_all_rows("zigzag two calls", two_calls=True)
+    _rank_fwd_bwd_all_rows(W.zigzag_rank(3), "zigzag", "zigzag two calls", active=[0, 1], two_calls=True)
 
 
-def test_balanced_rank_fwd_bwd_sampled():
+def test_balanced_rank_fwd_bwd_all_rows():
     """The same 128K sequence in the document-aware balanced layout (1024-row
-    chunks from sap_balance), rank 3: scattered Q chunks, all 8 ring steps."""
+    chunks from sap_balance), rank 3: scattered Q chunks, all 8 ring steps;
+    every row and key."""
     sap = _sap()
     from oracle import balance as B
     z = W.zigzag_rank(3)
     owner, _ = sap.sap_balance(z.cu, 8, 1024)
     assert owner.tolist() == B.balance(z.cu, 8, 1024)[0]
     w = W.owner_rank(z, owner.tolist(), 3, 1024, "balanced")
-    say(f"case balanced_sp8_128k_gqa_rank3 fwd+bwd ({len(w.q_segs)} Q segments), sampled rows")
-    _rank_fwd_bwd_sampled(w, "balanced")
+    say(f"case balanced_sp8_128k_gqa_rank3 fwd+bwd ({len(w.q_segs)} Q segments), every row and key")
+    _rank_fwd_bwd_all_rows(w, "balanced", "balanced", active=None)
 
 
 def test_plans_without_pairs_launch_nothing():
