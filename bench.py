@@ -57,6 +57,10 @@ KERNEL_SOURCE = {"attn_fwd": "attn_fwd.hip", "attn_bwd_kv": "attn_bwd.hip", "att
 
 def _args():
     ap = argparse.ArgumentParser()
+    ap.add_argument("--counters-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn the counter files of two rocprofv3 --pmc runs (FETCH_SIZE, then "
+                         "WRITE_SIZE) of 'bench.py --steps 3 --warmup 1 --no-ranks --no-workloads --no-cpu-baseline "
+                         "--calibration-copy-mib 1024' into profiles/<kernel>_<workload>_traffic.json records")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
@@ -85,6 +89,124 @@ def _traffic_from_profiles(kernel: str, workload: str):
     if rec.get("source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
         return None
     return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# HBM traffic records from rocprofv3 counter files
+
+COUNTER_RUN = ("python3 bench.py --steps 3 --warmup 1 --no-ranks --no-workloads --no-cpu-baseline "
+               "--calibration-copy-mib 1024")
+
+
+def _read_counter_csv(path, counter):
+    """{dispatch id: (kernel name, value in KiB)} of one rocprofv3 counter file."""
+    import csv
+    out = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        did = int(r["Dispatch_Id"])
+        name, val = r["Kernel_Name"], float(r["Counter_Value"])
+        prev = out.get(did, (name, 0.0))[1]
+        out[did] = (name, prev + val)          # summed over the counter's instances
+    return dict(sorted(out.items()))
+
+
+def _algorithmic_bytes(w):
+    """Bytes each kernel must move per launch at the least (each operand read
+    or written once), averaged over the launches of one step of the rank:
+    the forward's ring steps (fused merges), the backward's dK / dV and dQ
+    passes of each non-empty ring step."""
+    import long_context_sequence_doc_amd as sap
+    d, hq, hkv = w.d, w.hq, w.hkv
+    def rows_of(plan):
+        touched, desc = sap.sap_plan_q_tiles(plan)
+        return int(desc[touched, 1].sum())
+    fwd, kv, dq = [], [], []
+    first = True
+    for st in w.steps:
+        pf = sap.sap_plan(w.cu, w.q_segs, st.kv_segs, 128, 64)
+        inf = sap.sap_plan_info(pf)
+        if inf["n_tiles"] == 0:
+            continue
+        qr, kr = rows_of(pf), inf["n_touched_kv_tiles"] * 64
+        o_bytes = qr * hq * (4 * d + 4) * (1 if first else 2)      # O + LSE written (merging steps also read)
+        fwd.append(qr * hq * d * 2 + kr * hkv * d * 2 * 2 + o_bytes)
+        pb = sap.sap_plan(w.cu, w.q_segs, st.kv_segs, 64, 128)
+        ib = sap.sap_plan_info(pb)
+        qb, kb = rows_of(pb), ib["n_touched_kv_tiles"] * 128
+        reads = qb * hq * d * 2 * 2 + kb * hkv * d * 2 * 2 + qb * hq * 4 * 2     # Q, dO, K, V, LSE, D
+        kv.append(reads + kb * hkv * d * 4 * 2 * 2)                              # dK, dV read and written
+        dq.append(reads + qb * hq * d * 4 * 2)                                   # dQ read and written
+        first = False
+    avg = lambda x: int(round(sum(x) / len(x)))
+    return {"attn_fwd": avg(fwd), "attn_bwd_kv": avg(kv), "attn_bwd_dq": avg(dq)}, len(fwd)
+
+
+def counters_summary(fetch_csv, write_csv, workload="zigzag", warmup=1, steps=3, calib_mib=1024):
+    """HBM bytes per launch of the forward and the two backward passes from
+    FETCH_SIZE / WRITE_SIZE counter runs of COUNTER_RUN, scaled by what the
+    same counters read for the run's plain calibration copy of calib_mib MiB
+    (a copy that reads and writes calib_mib MiB), written to
+    profiles/<kernel>_<workload>_traffic.json with the hash of the kernel's
+    source. The forward's launches are the first ones of the run (the
+    headline step: warm-up and timed steps, one launch per non-empty ring
+    step); the backward's are the last ones (the training step as ring
+    steps, run last)."""
+    import workloads as W
+    w = W.by_name(workload)
+    fetch = _read_counter_csv(fetch_csv, "FETCH_SIZE")
+    write = _read_counter_csv(write_csv, "WRITE_SIZE")
+    kib = calib_mib * 1024.0
+    def calib(table):
+        vals = [v for n, v in table.values() if "copyBuffer" in n and v > 0.25 * kib]
+        if not vals:
+            raise SystemExit("no calibration copy in the counter file (run with --calibration-copy-mib)")
+        return vals[0]
+    fs, ws = kib / calib(fetch), kib / calib(write)
+    alg, n_steps = _algorithmic_bytes(w)
+    per_phase = (warmup + steps) * n_steps
+    out = []
+    for key, pattern, src, which in (("attn_fwd", "attn_fwd_kernel", "attn_fwd.hip", "first"),
+                                     ("attn_bwd_kv", "attn_bwd_kv_kernel", "attn_bwd.hip", "last"),
+                                     ("attn_bwd_dq", "attn_bwd_dq_kernel", "attn_bwd.hip", "last")):
+        fv = [v for n, v in fetch.values() if pattern in n]
+        wv = [v for n, v in write.values() if pattern in n]
+        if len(fv) < per_phase or len(wv) < per_phase:
+            raise SystemExit(f"{key}: {len(fv)} / {len(wv)} dispatches, expected at least {per_phase}")
+        fv = fv[:per_phase] if which == "first" else fv[-per_phase:]
+        wv = wv[:per_phase] if which == "first" else wv[-per_phase:]
+        by_step_f = [sum(fv[i::n_steps]) / (warmup + steps) for i in range(n_steps)]
+        by_step_w = [sum(wv[i::n_steps]) / (warmup + steps) for i in range(n_steps)]
+        bpl = (sum(fv) / per_phase * fs + sum(wv) / per_phase * ws) * 1024.0
+        rec = {
+            "kernel": key, "workload": w.name,
+            "what": f"HBM bytes per {key} launch, averaged over the {n_steps} non-empty ring-step launches of one step "
+                    f"({'the headline forward, merges in the epilogue' if key == 'attn_fwd' else 'the training step backward'})",
+            "commands": [f"cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/gpurun_out/pmc/fetch "
+                         f"-o fetch -- {COUNTER_RUN.replace('bench.py', '<repo>/bench.py')}",
+                         f"cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <repo>/gpurun_out/pmc/write "
+                         f"-o write -- {COUNTER_RUN.replace('bench.py', '<repo>/bench.py')}",
+                         "python3 bench.py --counters-summary <fetch csv> <write csv>"],
+            "calibration": {"kernel": f"__amd_rocclr_copyBuffer (a plain copy of {calib_mib} MiB)", "true_kib_read": kib,
+                            "true_kib_written": kib, "FETCH_SIZE_kib": calib(fetch), "WRITE_SIZE_kib": calib(write),
+                            "fetch_scale": round(fs, 4), "write_scale": round(ws, 4)},
+            "raw_kib_per_launch_by_ring_step": {"FETCH_SIZE": [round(x, 1) for x in by_step_f],
+                                                "WRITE_SIZE": [round(x, 1) for x in by_step_w]},
+            "dispatches_used": f"the {which} {per_phase} {pattern} dispatches of the run",
+            "bytes_per_launch": int(round(bpl)),
+            "algorithmic_bytes_per_launch": alg[key],
+            "traffic_over_algorithmic": round(bpl / alg[key], 3),
+            "source_sha256": hashlib.sha256(open(os.path.join(ROOT, "long_context_sequence_doc_amd", "csrc", src),
+                                                 "rb").read()).hexdigest(),
+        }
+        path = os.path.join(ROOT, "profiles", f"{key}_{w.name}_traffic.json")
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        out.append((path, rec["bytes_per_launch"], alg[key]))
+    for path, b, a in out:
+        print(f"{path}: {b / 1e6:.1f} MB per launch, algorithmic {a / 1e6:.1f} MB ({b / a:.2f}x)")
 
 
 # ---------------------------------------------------------------------------
@@ -467,6 +589,9 @@ def other_workloads(a, stream, skip):
 
 def main():
     a = _args()
+    if a.counters_summary:
+        counters_summary(*a.counters_summary, workload=a.workload)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {a.gpus}): every run here uses a single MI355X; "
               f"run it with --gpus 1", file=sys.stderr)
