@@ -78,15 +78,29 @@ def _args():
     return ap.parse_args()
 
 
+def _sources_sha256(kernel: str):
+    """Hash of what decides a kernel's HBM traffic: its source and the host
+    planner (tile lists, work order and chunking); None if a file is missing."""
+    csrc = os.path.join(ROOT, "long_context_sequence_doc_amd", "csrc")
+    h = hashlib.sha256()
+    for name in (KERNEL_SOURCE.get(kernel, kernel + ".hip"), "planner.cpp"):
+        path = os.path.join(csrc, name)
+        if not os.path.exists(path):
+            return None
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
+
+
 def _traffic_from_profiles(kernel: str, workload: str):
     """HBM bytes per launch recorded by rocprofv3 counter runs, if they were
-    taken on the current kernel source (its hash is stored with them)."""
+    taken on the current kernel source and planner (their hash is stored with
+    them)."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
-    src = os.path.join(ROOT, "long_context_sequence_doc_amd", "csrc", KERNEL_SOURCE.get(kernel, kernel + ".hip"))
-    if not (os.path.exists(path) and os.path.exists(src)):
+    if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+    sha = _sources_sha256(kernel)
+    if sha is None or rec.get("sources_sha256") != sha:
         return None
     return rec.get("bytes_per_launch")
 
@@ -197,8 +211,8 @@ def counters_summary(fetch_csv, write_csv, workload="zigzag", warmup=1, steps=3,
             "bytes_per_launch": int(round(bpl)),
             "algorithmic_bytes_per_launch": alg[key],
             "traffic_over_algorithmic": round(bpl / alg[key], 3),
-            "source_sha256": hashlib.sha256(open(os.path.join(ROOT, "long_context_sequence_doc_amd", "csrc", src),
-                                                 "rb").read()).hexdigest(),
+            "sources": [f"long_context_sequence_doc_amd/csrc/{src}", "long_context_sequence_doc_amd/csrc/planner.cpp"],
+            "sources_sha256": _sources_sha256(key),
         }
         path = os.path.join(ROOT, "profiles", f"{key}_{w.name}_traffic.json")
         with open(path, "w") as f:

@@ -241,43 +241,74 @@ sap_status build_plan(const int32_t *cu_in, int32_t n_docs, const sap_segment *q
     int32_t ki = kv_touched[size_t(i)];
     return kv_ptr[size_t(ki) + 1] - kv_ptr[size_t(ki)];
   });
-  // Chunks of at most `per` partners: at least ~kTargetChunks chunks over the
-  // plan (times the KV heads = workgroups of the dK / dV pass), none shorter
-  // than kMinChunk partners unless the tile itself is.
+  // Chunks: a KV tile's partner list (ascending Q tile) is cut where the Q
+  // tile index crosses a multiple of `per`, so the chunks of different KV
+  // tiles in one bin stream the same Q / dO rows; a piece shorter than per / 2
+  // joins the next one (the last joins the one before). `per` keeps about
+  // kTargetChunks bins over the plan (times the KV heads = workgroups of the
+  // dK / dV pass) and at least kMinChunk partners in each.
   constexpr int64_t kTargetChunks = 128, kMinChunk = 8;
   const int64_t per = std::max<int64_t>(kMinChunk, (n_tiles + kTargetChunks - 1) / kTargetChunks);
   std::vector<WorkItem> cw;
   std::vector<WorkRange> cr;
-  std::vector<int32_t> cs;
+  std::vector<int32_t> cs, cbin;
   P.kv_reduce.clear();
   P.n_kv_slots = 0;
+  std::vector<std::pair<int64_t, int64_t>> runs;
   for (int32_t oi : order) {
     const int32_t ki = kv_touched[size_t(oi)];
     const TileDesc &kt = P.kv_tiles[size_t(ki)];
     const WorkItem item{kt.local_start, kt.n, kt.global_start, ki};
     const int64_t begin = int64_t(P.kv_partners.size());
-    const int64_t cnt = kv_ptr[size_t(ki) + 1] - kv_ptr[size_t(ki)];
-    for (int64_t t = kv_ptr[size_t(ki)]; t < kv_ptr[size_t(ki) + 1]; ++t) {
+    const int64_t t0 = kv_ptr[size_t(ki)], cnt = kv_ptr[size_t(ki) + 1] - t0;
+    // partners listed from the last Q tile down: the chunks of one bin all
+    // start at its last Q tile (they differ only in where the diagonal ends
+    // them), so workgroups of a bin read each Q / dO tile at about the same
+    // time
+    for (int64_t t = t0 + cnt - 1; t >= t0; --t) {
       const TileDesc &qt = P.q_tiles[size_t(tr_q[size_t(t)])];
       P.kv_partners.push_back(PartnerEntry{qt.local_start, qt.global_start, qt.n, tr_c[size_t(t)]});
     }
-    const int64_t nch = (cnt + per - 1) / per;
-    if (nch == 1) {
+    auto bin = [&](int64_t i) { return int64_t(tr_q[size_t(t0 + i)]) / per; };
+    runs.clear();
+    for (int64_t i = 1, rb = 0; i <= cnt; ++i) {
+      if (i < cnt && bin(i) == bin(i - 1)) continue;
+      if (!runs.empty() && runs.back().second - runs.back().first < per / 2) runs.back().second = i;
+      else runs.emplace_back(rb, i);
+      rb = i;
+    }
+    if (runs.size() > 1 && runs.back().second - runs.back().first < per / 2) {
+      runs[runs.size() - 2].second = runs.back().second;
+      runs.pop_back();
+    }
+    if (runs.size() == 1) {
       cw.push_back(item);
       cr.push_back(WorkRange{int32_t(begin), int32_t(cnt)});
       cs.push_back(-1);
+      cbin.push_back(int32_t(bin(cnt - 1)));
       continue;
     }
-    P.kv_reduce.push_back(ReduceItem{kt.local_start, kt.n, P.n_kv_slots, int32_t(nch)});
-    for (int64_t c = 0; c < nch; ++c) {
-      const int64_t b = begin + c * cnt / nch, e = begin + (c + 1) * cnt / nch;
+    P.kv_reduce.push_back(ReduceItem{kt.local_start, kt.n, P.n_kv_slots, int32_t(runs.size())});
+    for (const auto &r : runs) {
       cw.push_back(item);
-      cr.push_back(WorkRange{int32_t(b), int32_t(e - b)});
+      // run [first, second) of the ascending list, in the descending one
+      cr.push_back(WorkRange{int32_t(begin + cnt - r.second), int32_t(r.second - r.first)});
       cs.push_back(P.n_kv_slots++);
+      cbin.push_back(int32_t(bin(r.second - 1)));
     }
   }
-  // heaviest chunk first
-  std::vector<int32_t> corder = lpt_order(cw.size(), [&](int32_t i) { return int64_t(cr[size_t(i)].count); });
+  // Chunks of at least per / 2 partners first, by bin (workgroups that run
+  // side by side on an XCD then stream the same Q / dO rows), the lighter
+  // ones after them, heaviest first.
+  std::vector<int32_t> corder(cw.size());
+  std::iota(corder.begin(), corder.end(), 0);
+  auto light = [&](int32_t i) { return int64_t(cr[size_t(i)].count) < per / 2; };
+  std::stable_sort(corder.begin(), corder.end(), [&](int32_t x, int32_t y) {
+    const bool lx = light(x), ly = light(y);
+    if (lx != ly) return ly;
+    if (lx) return cr[size_t(x)].count > cr[size_t(y)].count;
+    return cbin[size_t(x)] < cbin[size_t(y)];
+  });
   for (int32_t i : corder) {
     P.kv_work.push_back(cw[size_t(i)]);
     P.kv_range.push_back(cr[size_t(i)]);

@@ -293,22 +293,19 @@ def test_training_fwd_bwd_all_rows():
 
 
 def _heaviest_kv_tile_keys(rb, step_kv_segs):
-    """Local rows of the KV tile with the most partner Q tiles over the
-    backward's plans, and that count. The planner splits a KV tile into
-    chunks of at most max(8, ceil(n_tiles / 128)) partners; the tile found
-    here is asserted to be split, so its keys' dK / dV go through the
-    workspace slots and the ordered reduce."""
-    import long_context_sequence_doc_amd as sap
+    """Local rows of the split KV tile with the most partner Q tiles over the
+    backward's plans, and that count. A split tile's dK / dV are partial sums
+    in workspace slots that the ordered reduce adds up (the split rule is
+    written out in tests/kv_chunks.py)."""
     from oracle import planner as PL
-    best, keys, per = -1, [], 0
+    from tests.kv_chunks import kv_chunks
+    best, keys = -1, []
     for i in rb.active:
-        _, kt, _ = sap.sap_plan_tiles(rb.plans[i])
-        cnt = np.bincount(kt)
-        t = int(cnt.argmax())
-        if cnt[t] > best:
-            ls, nr, _ = PL.tiles_of(step_kv_segs[i], 128)[t]
-            best, keys, per = int(cnt[t]), list(range(ls, ls + nr)), max(8, -(-len(kt) // 128))
-    assert best > per, "the heaviest KV tile is not split"
+        for t, runs in kv_chunks(rb.plans[i]).items():
+            if len(runs) > 1 and sum(runs) > best:
+                ls, nr, _ = PL.tiles_of(step_kv_segs[i], 128)[t]
+                best, keys = sum(runs), list(range(ls, ls + nr))
+    assert best > 0, "no KV tile of the backward plans is split"
     return best, keys
 
 

@@ -108,3 +108,47 @@ def test_balanced_rank_plans_exact():
 def test_balance_rejects_bad_arguments(cu, p, chunk):
     with pytest.raises(sap.SapError):
         sap.sap_balance(cu, p, chunk)
+
+
+def _slots_from_workspace(plan) -> int:
+    # hq = 0 (no row terms), hkv = 1, d = 64: 2 x slots x 128 x 64 fp32
+    return sap.sap_attn_bwd_workspace(plan, 0, 1, 64) // (2 * 128 * 64 * 4)
+
+
+@pytest.mark.parametrize("name", ["tiny", "ring", "zigzag", "train"])
+def test_backward_chunk_rule_matches_library(name):
+    """The dK / dV pass's split, written out in tests/kv_chunks.py, gives the
+    library's workspace slot count on every backward plan (64 x 128 tiles) of
+    the workloads, in the ring and the one-call forms; at least one of them
+    splits tiles."""
+    from tests.kv_chunks import n_slots
+    w = W.by_name(name)
+    plans = [sap.sap_plan(w.cu, w.q_segs, st.kv_segs, 64, 128) for st in w.steps]
+    all_kv = [seg for st in w.steps for seg in st.kv_segs]
+    plans.append(sap.sap_plan(w.cu, w.q_segs, all_kv, 64, 128))
+    for p in plans:
+        assert n_slots(p) == _slots_from_workspace(p)
+    if name in ("zigzag", "ring"):
+        assert any(_slots_from_workspace(p) > 0 for p in plans)
+
+
+def test_backward_chunk_rule_random_layouts():
+    """Same on random document layouts with long documents (a KV tile meets
+    many Q tiles, so splits and merged short pieces both occur)."""
+    from tests.kv_chunks import kv_chunks, n_slots
+    rng = np.random.default_rng(11)
+    seen_split = seen_merge = False
+    for _ in range(12):
+        lens = rng.integers(1, 6000, size=int(rng.integers(1, 6)))
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(int).tolist()
+        total = cu[-1]
+        cut = int(rng.integers(0, total))
+        for q_segs, kv_segs in (([(0, total, 0)], [(0, total, 0)]),
+                                ([(cut, total, 0)], [(0, cut, 0)] if cut else [])):
+            p = sap.sap_plan(cu, q_segs, kv_segs, 64, 128)
+            assert n_slots(p) == _slots_from_workspace(p)
+            ch = kv_chunks(p)
+            seen_split |= any(len(r) > 1 for r in ch.values())
+            per = max(8, -(-sap.sap_plan_info(p)["n_tiles"] // 128))
+            seen_merge |= any(r > per for rs in ch.values() for r in rs)
+    assert seen_split and seen_merge
