@@ -320,10 +320,6 @@ __global__ __launch_bounds__(NTK) void attn_bwd_kv_kernel(BwdParams p) {
     unsigned char *cur = lds + ST0 + (itr & 1) * STAGE;
     unsigned char *nxt = lds + ST0 + ((itr + 1) & 1) * STAGE;
     const bool more = itr + 1 < n_iter;
-    if (more) {
-      issue_rows(itr + 1, nxt);
-      if (tid < BMB) load_terms(itr + 1);
-    }
 
     // ---- S = Q K^T, dP = dO V^T (this wave's 32 rows x 32 keys)
     f32x16 sacc = f32x16{}, pacc = f32x16{};
@@ -343,6 +339,14 @@ __global__ __launch_bounds__(NTK) void attn_bwd_kv_kernel(BwdParams p) {
         pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, bv, pacc, 0, 0, 0);
         aq = naq; ad = nad; bk = nbk; bv = nbv;
       }
+    }
+
+    // the next stage's copies and row terms, issued while the matrix cores
+    // work through S and dP (all waves issue them at the same point, and the
+    // memory pipeline takes them in turn)
+    if (more) {
+      issue_rows(itr + 1, nxt);
+      if (tid < BMB) load_terms(itr + 1);
     }
 
     // ---- P and dS; accumulator element i is query row
