@@ -693,8 +693,6 @@ __global__ __launch_bounds__(128 * NH) void attn_bwd_dq_kernel(BwdParams p) {
       nit = it + 1;
       nhalf = 0;
     }
-    if (nit < rg.count) issue_half(entry(nit), nhalf, lds + (stage_i ^ 1) * STAGE);
-
     const int k0 = half * HKQ;                    // first key of this part within the tile
     const int kn = min(HKQ, kt.n - k0);           // keys in this part
 
@@ -755,6 +753,11 @@ __global__ __launch_bounds__(128 * NH) void attn_bwd_dq_kernel(BwdParams p) {
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[t], sacc, 0, 0, 0);
         pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[t], pacc, 0, 0, 0);
       }
+      // the next half's copies, issued while the matrix cores work through
+      // the first block's S^T and dP^T (all waves issue them at the same
+      // point, and the memory pipeline takes them in turn)
+      if constexpr (kb == 0)
+        if (nit < rg.count) issue_half(entry(nit), nhalf, lds + (stage_i ^ 1) * STAGE);
       // ---- dS^T = P^T o (dP^T - D); element i is key k0 + kb*32 + 8*(i/4) + 4*hf + (i%4)
       bf16x8 sb[2];
       auto ds_t = [&](auto mask_tag) {
