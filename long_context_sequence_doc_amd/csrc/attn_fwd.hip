@@ -151,6 +151,27 @@ __device__ inline void issue_half(const FwdParams &p, const PartnerEntry &pe, in
                                      16, 0, 0);
 }
 
+// The same copies issued by four waves of an eight-wave workgroup (c = 0..3
+// numbers them): chunk position P = (i * 4 + c) * 64 + lane, offsets
+// computed here (nothing held in registers across the loop).
+template <int D, int NT, bool V>
+__device__ inline void issue_half_by4(const FwdParams &p, const PartnerEntry &pe, int g, unsigned char *stage, int c,
+                                      int lane) {
+  using G = Stage<D, NT>;
+  constexpr int L4 = BN * G::CPR / 256;
+  const int64_t base = int64_t(pe.local_start) * p.kv_row_stride + int64_t(g) * D;
+  const unsigned short *src = (V ? p.v : p.k) + base;
+  const int stride = int(p.kv_row_stride);
+#pragma unroll
+  for (int i = 0; i < L4; ++i) {
+    const int P = (i * 4 + c) * 64 + lane;
+    const int row = P / G::CPR, pos = P % G::CPR;
+    const int off = min(row, pe.n - 1) * stride + 8 * (pos ^ (V ? G::vsw(row) : G::ksw(row)));
+    __builtin_amdgcn_global_load_lds((global_void *)(src + off), (lds_void *)(stage + (V ? G::TILE : 0) + (i * 4 + c) * 1024),
+                                     16, 0, 0);
+  }
+}
+
 __device__ inline bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
 // max / sum of a lane's value and that of lane ^ 32, the same in both lanes.
@@ -362,6 +383,11 @@ __global__ __launch_bounds__(2 * TM * NH) __attribute__((amdgpu_waves_per_eu(2))
     // slot), turns S_j into P_j on the vector ALUs while the matrix cores
     // compute S_{j+1}, adds V_j P_j into O, and ends at a barrier that makes
     // its copies visible and frees the slots it read.
+    // waves 1, 3, 4, 6: one of each pair (w, w + 4) and of each pair
+    // (2i, 2i + 1), whichever pairs share a SIMD
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const bool copier = ((wave_u >> 2) ^ wave_u) & 1;
+    const int copier_id = wave_u >> 1;
     PartnerEntry e2 = uniform(raw(2));
     issue_half<D, NT, false>(p, e0, g, lds, wave, lane, full_offs);
     issue_half<D, NT, true>(p, e0, g, lds, wave, lane, full_offs);
@@ -375,8 +401,12 @@ __global__ __launch_bounds__(2 * TM * NH) __attribute__((amdgpu_waves_per_eu(2))
       constexpr bool HN = decltype(has_next)::value;
       unsigned char *stage_j = lds + (j & 1) * ST::BYTES;
       unsigned char *stage_n = lds + ((j + 1) & 1) * ST::BYTES;
-      if (j + 2 < cnt) issue_half<D, NT, false>(p, e2, g, stage_j, wave, lane, full_offs);
-      if (HN) issue_half<D, NT, true>(p, e1, g, stage_n, wave, lane, full_offs);
+      // one wave of each pair that shares a SIMD issues the copies (twice as
+      // many); its partner starts on the tile meanwhile
+      if (copier) {
+        if (j + 2 < cnt) issue_half_by4<D, NT, false>(p, e2, g, stage_j, copier_id, lane);
+        if (HN) issue_half_by4<D, NT, true>(p, e1, g, stage_n, copier_id, lane);
+      }
       const PartnerEntry raw3 = raw(j + 3);
       tile_math(s, e0, stage_j, [&] {
         if (HN) scores(s_next, stage_n);
