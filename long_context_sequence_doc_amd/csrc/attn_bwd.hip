@@ -26,12 +26,17 @@
 //   blocks' dK / dV partial sums are added through LDS at the end and
 //   written once. Two waves per SIMD (each holds only its keys' dK^T / dV^T
 //   accumulators). KV tiles with many partners are split into several
-//   chunks by the planner (so the pass has enough workgroups); their chunks
-//   store partial sums in workspace slots and bwd_kv_reduce_kernel adds the
-//   slots up in order, so the result stays deterministic.
+//   chunks by the planner (so the pass has enough workgroups), cut on a
+//   fixed grid of Q tiles and walked from the last Q tile down, so the
+//   workgroups an XCD runs side by side stream the same Q / dO rows through
+//   its L2; split tiles' chunks store partial sums in workspace slots and
+//   bwd_kv_reduce_kernel adds the slots up in order, so the result stays
+//   deterministic. Each iteration issues the next stage's copies after its
+//   S / dP products, so the waves' wait for the memory pipeline to take them
+//   runs beside the matrix work.
 //
-// attn_bwd_dq_kernel -- dQ. One workgroup = one 64-row Q tile x one or two
-//   query heads of a KV head; 2 waves per head own 32 query rows each and
+// attn_bwd_dq_kernel -- dQ. One workgroup = one 64-row Q tile x one, two or
+//   four query heads of a KV head; 2 waves per head own 32 query rows each and
 //   walk the KV tiles that meet the Q tile, in 64-key (or, with one head,
 //   32-key) parts copied straight into a double-buffered LDS stage shared by
 //   the heads. As in the forward,

@@ -35,7 +35,9 @@
 //     of V: while the vector ALUs turn tile j's scores into P_j, the matrix
 //     cores already compute tile j+1's scores (the two waves a SIMD holds
 //     are barrier-locked in the same phase, so without this the matrix
-//     cores idle through the softmax). Four-wave workgroups (several per CU)
+//     cores idle through the softmax); in that loop one wave of each pair
+//     sharing a SIMD issues the tile copies, twice as many, while its
+//     partner starts on the tile. Four-wave workgroups (several per CU)
 //     keep the plain double buffer.
 //   * Online softmax in fp32 with exp2 and the scale folded into one FMA.
 //     The running max is only moved (and O, l rescaled) when it grows by
