@@ -57,7 +57,8 @@ def _bwd_call(sap, cu, q_segs, kv_segs, qd, kd, vd, dod, o, lse, hq, hkv, d, sca
 def test_random_small_layouts(seed):
     """Ragged tiles, 1-token and empty documents, GQA (group sizes 1-4; odd
     and even groups take different workgroup shapes), D in {64, 128}, a
-    sharded Q (two segments, local != global rows) and KV in two pieces."""
+    sharded Q (two segments, local != global rows), KV in two pieces and, on
+    odd seeds, K / V rows strided past their heads."""
     sap = _sap()
     import torch
     rng = np.random.default_rng(700 + seed)
@@ -80,17 +81,20 @@ def test_random_small_layouts(seed):
     qf, kf, vf, dof = mk(hq), mk(hkv), mk(hkv), mk(hq)
     ql = np.zeros((len(gq), hq, d), dtype=np.uint16)
     dol = np.zeros((len(gq), hq, d), dtype=np.uint16)
-    kl = np.zeros((len(gk), hkv, d), dtype=np.uint16)
-    vl = np.zeros((len(gk), hkv, d), dtype=np.uint16)
+    # K / V rows padded by an extra head on odd seeds (kv_row_stride > hkv * d)
+    kpad = hkv + (seed % 2)
+    kl = np.zeros((len(gk), kpad, d), dtype=np.uint16)
+    vl = np.zeros((len(gk), kpad, d), dtype=np.uint16)
     vq, vk = gq >= 0, gk >= 0
     ql[vq], dol[vq] = qf[gq[vq]], dof[gq[vq]]
-    kl[vk], vl[vk] = kf[gk[vk]], vf[gk[vk]]
+    kl[vk, :hkv], vl[vk, :hkv] = kf[gk[vk]], vf[gk[vk]]
     gq0 = np.where(vq, gq, 0)
     gk0 = np.where(vk, gk, -10 ** 9)
+    k64, v64 = f64(kl[:, :hkv]), f64(vl[:, :hkv])
     # final O / LSE from the oracle over this call's KV (= all keys here)
-    o_ref, lse_ref = A.forward(f64(ql), f64(kl), f64(vl), gq0, gk0, cu, scale)
+    o_ref, lse_ref = A.forward(f64(ql), k64, v64, gq0, gk0, cu, scale)
     rows = np.nonzero(vq)[0]
-    dq_ref, dk_ref, dv_ref = A.backward(f64(ql), f64(kl), f64(vl), f64(dol), o_ref, lse_ref, gq0, gk0, cu, scale)
+    dq_ref, dk_ref, dv_ref = A.backward(f64(ql), k64, v64, f64(dol), o_ref, lse_ref, gq0, gk0, cu, scale)
     qd, kd, vd, dod = to_dev(ql), to_dev(kl), to_dev(vl), to_dev(dol)
     o = torch.from_numpy(o_ref.astype(np.float32)).cuda()
     lse = torch.from_numpy(lse_ref.astype(np.float32)).cuda()

@@ -87,8 +87,8 @@ def test_tiny_full_sequence():
 @pytest.mark.parametrize("seed", range(10))
 def test_random_small_layouts(seed, block_m):
     """Ragged tiles, 1-token and empty documents, GQA, D in {64, 128},
-    non-contiguous segments, strided Q rows, 128- and 256-row Q tiles;
-    untouched rows stay NaN."""
+    non-contiguous segments, strided Q rows (and, on odd seeds, strided K / V
+    rows), 128- and 256-row Q tiles; untouched rows stay NaN."""
     sap = _sap()
     rng = np.random.default_rng(900 + seed)
     d = 128 if seed % 2 else 64
@@ -114,9 +114,11 @@ def test_random_small_layouts(seed, block_m):
     # local buffers; Q gets an extra padding head so its row stride exceeds hq*d
     ql = np.zeros((len(gq), hq + 1, d), dtype=np.uint16)
     ql[gq >= 0, :hq] = qf[gq[gq >= 0]]
-    kl = np.zeros((len(gk), hkv, d), dtype=np.uint16)
-    vl = np.zeros((len(gk), hkv, d), dtype=np.uint16)
-    kl[gk >= 0], vl[gk >= 0] = kf[gk[gk >= 0]], vf[gk[gk >= 0]]
+    # K / V rows padded by an extra head on odd seeds (kv_row_stride > hkv * d)
+    kpad = hkv + (seed % 2)
+    kl = np.zeros((len(gk), kpad, d), dtype=np.uint16)
+    vl = np.zeros((len(gk), kpad, d), dtype=np.uint16)
+    kl[gk >= 0, :hkv], vl[gk >= 0, :hkv] = kf[gk[gk >= 0]], vf[gk[gk >= 0]]
     import torch
     plan = sap.sap_plan(cu, q_segs, kv_segs, block_m, 64)
     info = sap.sap_plan_info(plan)
@@ -135,7 +137,7 @@ def test_random_small_layouts(seed, block_m):
     assert np.isnan(o[untouched]).all() and np.isnan(lse[:, untouched]).all(), "wrote outside touched tiles"
     q64 = np.zeros((len(gq), hq, d))
     q64[valid] = f64(qf[gq[valid]])
-    ro, rl = A.forward(q64, f64(kl), f64(vl), np.where(gq >= 0, gq, 0), np.where(gk >= 0, gk, -10**9), cu,
+    ro, rl = A.forward(q64, f64(kl[:, :hkv]), f64(vl[:, :hkv]), np.where(gq >= 0, gq, 0), np.where(gk >= 0, gk, -10**9), cu,
                        1.0 / np.sqrt(d), rows=rows)
     compare(o, lse, ro, rl, rows=rows, label=f"random{seed}/{block_m}")
 
