@@ -35,11 +35,14 @@
 //   S / dP products, so the waves' wait for the memory pipeline to take them
 //   runs beside the matrix work.
 //
-// attn_bwd_dq_kernel -- dQ. One workgroup = one 64-row Q tile x one, two or
-//   four query heads of a KV head; 2 waves per head own 32 query rows each and
-//   walk the KV tiles that meet the Q tile, in 64-key (or, with one head,
-//   32-key) parts copied straight into a double-buffered LDS stage shared by
-//   the heads. As in the forward,
+// attn_bwd_dq_kernel -- dQ. One workgroup = one Q tile x one, two or four
+//   query heads of a KV head: with four heads the plan's 64-row Q tiles, with
+//   one or two its 128-row list (the same rows, paired; consecutive 64-row
+//   tiles nearly always meet the same 128-key KV tiles), so each staged K / V
+//   part serves at least 256 query rows x heads. One wave per 32 query rows
+//   and head; the waves walk the KV tiles that meet the Q tile, in 64-key (or,
+//   with two waves, 32-key) parts copied straight into a double-buffered LDS
+//   stage shared by the heads. As in the forward,
 //   S^T = K Q^T and dP^T = V dO^T put one query per lane pair, P^T and dS^T
 //   come out in the B-operand layout of dQ^T += K^T dS^T, whose K^T operand
 //   comes from transposing LDS reads. Each workgroup owns its dQ rows: the
@@ -588,14 +591,18 @@ constexpr int HK = 64;      // keys per half of a KV tile in the dQ kernel
 //   S^T = K Q^T, dP^T = V dO^T            (A: K / V rows, B: Q / dO in registers)
 //   dS^T = P^T o (dP^T - D)               (one query per lane pair: LSE, D scalars)
 //   dQ^T += K^T dS^T                      (A: K^T by transposing reads of K rows)
-template <int D, int NH>
-__global__ __launch_bounds__(128 * NH) void attn_bwd_dq_kernel(BwdParams p) {
+// TQ: rows of the Q tiles (64: the plan's own; 128: its 128-row list), one
+// wave per 32 rows and head.
+template <int D, int NH, int TQ>
+__global__ __launch_bounds__(2 * TQ * NH) void attn_bwd_dq_kernel(BwdParams p) {
   using RT = RowTile<D>;
-  constexpr int NTD = 128 * NH;                      // threads
-  constexpr int NWV = 2 * NH;                        // waves
-  // keys per stage: 64 (half a KV tile) with two heads per workgroup; 32 (a
-  // quarter) with one, so that four 2-wave workgroups fit a CU's LDS
-  constexpr int HKQ = NH >= 2 ? HK : HK / 2;
+  constexpr int WPH = TQ / 32;                       // waves per head
+  constexpr int NWV = WPH * NH;                      // waves
+  constexpr int NTD = 64 * NWV;                      // threads
+  // keys per stage: 64 (half a KV tile) with four or more waves per
+  // workgroup; 32 (a quarter) with two, so that four 2-wave workgroups fit
+  // a CU's LDS
+  constexpr int HKQ = NWV >= 4 ? HK : HK / 2;
   constexpr int KBQ = HKQ / 32;                      // 32-key blocks per stage
   constexpr int KOFF = 0, VOFF = HKQ * RT::ROW;      // K, V part-tiles (RowTile rows)
   constexpr int STAGE = 2 * HKQ * RT::ROW;
@@ -612,11 +619,11 @@ __global__ __launch_bounds__(128 * NH) void attn_bwd_dq_kernel(BwdParams p) {
   const int w = G / p.hkv, g = G % p.hkv;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
-  const int h = g * p.group + (slot % pairs) * NH + wave / 2;
+  const int h = g * p.group + (slot % pairs) * NH + wave / WPH;
   const WorkItem qt = p.work[w];
   const WorkRange rg = p.range[w];
 
-  const int my_row = (wave & 1) * 32 + l32;       // query row within the Q tile
+  const int my_row = (wave % WPH) * 32 + l32;     // query row within the Q tile
   const bool row_ok = my_row < qt.n;
   const int qrow = qt.local_start + min(my_row, qt.n - 1);
   const int qg = qt.global_start + my_row;
@@ -704,7 +711,7 @@ __global__ __launch_bounds__(128 * NH) void attn_bwd_dq_kernel(BwdParams p) {
     // The stage's keys go in 32-key blocks, each through S^T / dP^T, dS^T and
     // its dQ^T steps before the next, so only one block's score
     // accumulators are live (room for the unmasked path of FULL tiles).
-    const bool masked = kt.cls != SAP_TILE_FULL || kn < HKQ || qt.n < BMB;
+    const bool masked = kt.cls != SAP_TILE_FULL || kn < HKQ || qt.n < TQ;
     int lo = -(1 << 30), hi = kn - 1;             // allowed stage-local key range of this query
     if (masked) {
       if (kt.cls != SAP_TILE_FULL) hi = min(hi, qg - (kt.global_start + k0));
@@ -866,9 +873,14 @@ BwdParams bwd_params(const BwdLaunch &a) {
 
 // query heads per dQ workgroup and its workgroup count
 int dq_heads(int group) { return group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1; }
+// rows of its Q tiles: with four heads the plan's 64-row tiles; with one or
+// two its 128-row list (four waves per head, so each staged K / V part
+// serves twice the rows)
+int dq_rows(int group) { return dq_heads(group) == 4 ? 64 : 128; }
+int32_t dq_items(const BwdLaunch &a) { return dq_rows(a.hq / a.hkv) == 64 ? a.n_q_work : a.n_q2_work; }
 int64_t dq_blocks(const BwdLaunch &a) {
   const int group = a.hq / a.hkv;
-  const int64_t slots = (int64_t(a.n_q_work) * a.hkv + NXCD - 1) / NXCD;
+  const int64_t slots = (int64_t(dq_items(a)) * a.hkv + NXCD - 1) / NXCD;
   return slots * NXCD * (group / dq_heads(group));
 }
 
@@ -887,7 +899,8 @@ const char *attn_bwd_limits(const BwdLaunch &a) {
   const int64_t cap = int64_t(UINT32_MAX);
   if (int64_t(a.n_work) * a.hkv * NTK > cap) return "dK/dV grid too large (KV-tile chunks x KV heads)";
   if (int64_t(a.n_reduce) * a.hkv * NT > cap) return "split-tile reduce grid too large";
-  if (dq_blocks(a) * 128 * dq_heads(a.hq / a.hkv) > cap) return "dQ grid too large (Q tiles x query heads)";
+  if (dq_blocks(a) * 2 * dq_rows(a.hq / a.hkv) * dq_heads(a.hq / a.hkv) > cap)
+    return "dQ grid too large (Q tiles x query heads)";
   return nullptr;
 }
 
@@ -946,29 +959,29 @@ hipError_t launch_attn_bwd_dkdv(const BwdLaunch &a, hipStream_t stream) {
 }
 
 hipError_t launch_attn_bwd_dq(const BwdLaunch &a, hipStream_t stream) {
-  if (a.n_q_work <= 0) return hipSuccess;
+  if (dq_items(a) <= 0) return hipSuccess;
   if (attn_bwd_limits(a)) return hipErrorInvalidValue;
   BwdParams p = bwd_params(a);
-  p.work = a.q_work;
-  p.range = a.q_range;
-  p.partners = a.q_partners;
-  p.n_work = a.n_q_work;
-  const int nh = dq_heads(p.group);
-  const dim3 grid{static_cast<unsigned>(dq_blocks(a))};
+  const int nh = dq_heads(p.group), tq = dq_rows(p.group);
+  p.work = tq == 64 ? a.q_work : a.q2_work;
+  p.range = tq == 64 ? a.q_range : a.q2_range;
+  p.partners = tq == 64 ? a.q_partners : a.q2_partners;
+  p.n_work = dq_items(a);
+  const dim3 grid{static_cast<unsigned>(dq_blocks(a))}, block{static_cast<unsigned>(2 * tq * nh)};
   if (a.d == 128) {
     if (nh == 4)
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 4>), grid, dim3(512), 0, stream, p);
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 4, 64>), grid, block, 0, stream, p);
     else if (nh == 2)
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 2>), grid, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 2, 128>), grid, block, 0, stream, p);
     else
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 1>), grid, dim3(128), 0, stream, p);
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 1, 128>), grid, block, 0, stream, p);
   } else {
     if (nh == 4)
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 4>), grid, dim3(512), 0, stream, p);
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 4, 64>), grid, block, 0, stream, p);
     else if (nh == 2)
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 2>), grid, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 2, 128>), grid, block, 0, stream, p);
     else
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 1>), grid, dim3(128), 0, stream, p);
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 1, 128>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }

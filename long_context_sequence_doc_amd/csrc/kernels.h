@@ -58,10 +58,14 @@ struct BwdLaunch {
   const WorkRange *range;
   const PartnerEntry *partners;
   int32_t n_work;
-  const WorkItem *q_work;       // Q-major work (dQ)
+  const WorkItem *q_work;       // Q-major work (dQ) over the plan's 64-row Q tiles
   const WorkRange *q_range;
   const PartnerEntry *q_partners;
   int32_t n_q_work;
+  const WorkItem *q2_work;      // the same over 128-row Q tiles
+  const WorkRange *q2_range;
+  const PartnerEntry *q2_partners;
+  int32_t n_q2_work;
   const int32_t *ds_q;
   const int32_t *kv_slot;       // per KV-major chunk: workspace slot, -1 = owns its dK / dV rows
   const ReduceItem *kv_reduce;  // split KV tiles: slots to add up

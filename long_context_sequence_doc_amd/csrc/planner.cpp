@@ -314,6 +314,15 @@ sap_status build_plan(const int32_t *cu_in, int32_t n_docs, const sap_segment *q
     P.kv_range.push_back(cr[size_t(i)]);
     P.kv_slot.push_back(cs[size_t(i)]);
   }
+  if (bm == 64 && bn == 128) {
+    // the dQ pass's work over 128-row Q tiles (same segments, same KV tiles)
+    Plan P2;
+    const sap_status s2 = build_plan(cu_in, n_docs, q_segs, n_q, kv_segs, n_kv, 128, 128, &P2, err);
+    if (s2 != SAP_OK) return s2;
+    P.q2_work = std::move(P2.q_work);
+    P.q2_range = std::move(P2.q_range);
+    P.q2_partners = std::move(P2.q_partners);
+  }
   return SAP_OK;
 }
 

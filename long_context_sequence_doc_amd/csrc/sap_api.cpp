@@ -115,14 +115,16 @@ sap_status sap_plan_upload(sap_plan_t plan, void *hip_stream) {
   if (P.dev.base) return ok();
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   // one allocation; each table 256-byte aligned
-  constexpr int NT = 10;
+  constexpr int NT = 13;
   size_t off[NT], total = 0;
   const void *src[NT] = {P.q_work.data(), P.q_range.data(), P.q_partners.data(), P.kv_work.data(),
                          P.kv_range.data(), P.kv_partners.data(), P.ds_q.data(), P.touched_rows.data(),
-                         P.kv_slot.data(), P.kv_reduce.data()};
+                         P.kv_slot.data(), P.kv_reduce.data(), P.q2_work.data(), P.q2_range.data(),
+                         P.q2_partners.data()};
   size_t len[NT] = {bytes_of(P.q_work), bytes_of(P.q_range), bytes_of(P.q_partners), bytes_of(P.kv_work),
                     bytes_of(P.kv_range), bytes_of(P.kv_partners), bytes_of(P.ds_q), bytes_of(P.touched_rows),
-                    bytes_of(P.kv_slot), bytes_of(P.kv_reduce)};
+                    bytes_of(P.kv_slot), bytes_of(P.kv_reduce), bytes_of(P.q2_work), bytes_of(P.q2_range),
+                    bytes_of(P.q2_partners)};
   for (int i = 0; i < NT; ++i) {
     off[i] = total;
     total += align_up(std::max<size_t>(len[i], 1));
@@ -160,6 +162,9 @@ sap_status sap_plan_upload(sap_plan_t plan, void *hip_stream) {
   P.dev.touched_rows = reinterpret_cast<const int32_t *>(b + off[7]);
   P.dev.kv_slot = reinterpret_cast<const int32_t *>(b + off[8]);
   P.dev.kv_reduce = reinterpret_cast<const sap::ReduceItem *>(b + off[9]);
+  P.dev.q2_work = reinterpret_cast<const sap::WorkItem *>(b + off[10]);
+  P.dev.q2_range = reinterpret_cast<const sap::WorkRange *>(b + off[11]);
+  P.dev.q2_partners = reinterpret_cast<const sap::PartnerEntry *>(b + off[12]);
   P.dev.device = dev;
   return ok();
 }
@@ -342,6 +347,10 @@ void fill_bwd(const sap::Plan &P, sap::BwdLaunch *a) {
   a->q_range = P.dev.q_range;
   a->q_partners = P.dev.q_partners;
   a->n_q_work = int32_t(P.q_work.size());
+  a->q2_work = P.dev.q2_work;
+  a->q2_range = P.dev.q2_range;
+  a->q2_partners = P.dev.q2_partners;
+  a->n_q2_work = int32_t(P.q2_work.size());
   a->ds_q = P.dev.ds_q;
 }
 

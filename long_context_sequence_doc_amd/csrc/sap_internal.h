@@ -65,6 +65,9 @@ struct DeviceTables {
   const ReduceItem *kv_reduce = nullptr; // split KV tiles
   const int32_t *ds_q = nullptr;         // [tq] document start of each local Q row
   const int32_t *touched_rows = nullptr; // [n_touched] (local_start, n) pairs, ascending
+  const WorkItem *q2_work = nullptr;     // 128-row Q tiles (dQ pass), heaviest first
+  const WorkRange *q2_range = nullptr;
+  const PartnerEntry *q2_partners = nullptr;
   int device = -1;
 };
 
@@ -90,6 +93,12 @@ struct Plan {
   std::vector<ReduceItem> kv_reduce;
   int32_t n_kv_slots = 0;
   std::vector<int32_t> ds_q;
+  // A 64 x 128 plan (the backward's) also lists its work over 128-row Q
+  // tiles against the same 128-key KV tiles: the dQ pass of workgroups with
+  // one or two query heads streams each K / V part for twice the rows.
+  std::vector<WorkItem> q2_work;
+  std::vector<WorkRange> q2_range;
+  std::vector<PartnerEntry> q2_partners;
   std::vector<int32_t> touched;       // touched Q tile ids, ascending
   std::vector<int32_t> touched_rows;  // (local_start, n) of touched Q tiles, ascending
   int32_t n_touched_kv = 0;
