@@ -40,9 +40,9 @@
 //   one or two its 128-row list (the same rows, paired; consecutive 64-row
 //   tiles nearly always meet the same 128-key KV tiles), so each staged K / V
 //   part serves at least 256 query rows x heads. One wave per 32 query rows
-//   and head; the waves walk the KV tiles that meet the Q tile, in 64-key (or,
-//   with two waves, 32-key) parts copied straight into a double-buffered LDS
-//   stage shared by the heads. As in the forward,
+//   and head; the waves walk the KV tiles that meet the Q tile, in parts of
+//   128 keys (eight waves), 64 (four) or 32 (two) copied straight into a
+//   double-buffered LDS stage shared by the heads. As in the forward,
 //   S^T = K Q^T and dP^T = V dO^T put one query per lane pair, P^T and dS^T
 //   come out in the B-operand layout of dQ^T += K^T dS^T, whose K^T operand
 //   comes from transposing LDS reads. Each workgroup owns its dQ rows: the
@@ -599,10 +599,10 @@ __global__ __launch_bounds__(2 * TQ * NH) void attn_bwd_dq_kernel(BwdParams p) {
   constexpr int WPH = TQ / 32;                       // waves per head
   constexpr int NWV = WPH * NH;                      // waves
   constexpr int NTD = 64 * NWV;                      // threads
-  // keys per stage: 64 (half a KV tile) with four or more waves per
-  // workgroup; 32 (a quarter) with two, so that four 2-wave workgroups fit
-  // a CU's LDS
-  constexpr int HKQ = NWV >= 4 ? HK : HK / 2;
+  // keys per stage: a whole 128-key KV tile with eight waves per workgroup
+  // (one workgroup per CU, 128 KB of LDS; half the barriers per key); 64
+  // (half a tile) with four waves (two workgroups per CU); 32 with two (four)
+  constexpr int HKQ = NWV >= 8 ? 2 * HK : NWV >= 4 ? HK : HK / 2;
   constexpr int KBQ = HKQ / 32;                      // 32-key blocks per stage
   constexpr int KOFF = 0, VOFF = HKQ * RT::ROW;      // K, V part-tiles (RowTile rows)
   constexpr int STAGE = 2 * HKQ * RT::ROW;
