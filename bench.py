@@ -79,11 +79,12 @@ def _args():
 
 
 def _sources_sha256(kernel: str):
-    """Hash of what decides a kernel's HBM traffic: its source and the host
-    planner (tile lists, work order and chunking); None if a file is missing."""
+    """Hash of what decides a kernel's HBM traffic: its source, the shared
+    global -> LDS copy header and the host planner (tile lists, work order and
+    chunking); None if a file is missing."""
     csrc = os.path.join(ROOT, "long_context_sequence_doc_amd", "csrc")
     h = hashlib.sha256()
-    for name in (KERNEL_SOURCE.get(kernel, kernel + ".hip"), "planner.cpp"):
+    for name in (KERNEL_SOURCE.get(kernel, kernel + ".hip"), "lds_copy.h", "planner.cpp"):
         path = os.path.join(csrc, name)
         if not os.path.exists(path):
             return None
@@ -211,7 +212,8 @@ def counters_summary(fetch_csv, write_csv, workload="zigzag", warmup=1, steps=3,
             "bytes_per_launch": int(round(bpl)),
             "algorithmic_bytes_per_launch": alg[key],
             "traffic_over_algorithmic": round(bpl / alg[key], 3),
-            "sources": [f"long_context_sequence_doc_amd/csrc/{src}", "long_context_sequence_doc_amd/csrc/planner.cpp"],
+            "sources": [f"long_context_sequence_doc_amd/csrc/{src}", "long_context_sequence_doc_amd/csrc/lds_copy.h",
+                        "long_context_sequence_doc_amd/csrc/planner.cpp"],
             "sources_sha256": _sources_sha256(key),
         }
         path = os.path.join(ROOT, "profiles", f"{key}_{w.name}_traffic.json")

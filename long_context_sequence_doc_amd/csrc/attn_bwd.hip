@@ -56,6 +56,7 @@
 #include <type_traits>
 
 #include "kernels.h"
+#include "lds_copy.h"
 
 // Device scratch of the allocation-free backward (sap_attn_bwd_noalloc): the
 // row terms and split-tile partial sums that sap_attn_bwd keeps in the
@@ -77,8 +78,6 @@ typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void global_void;
 
 constexpr int BMB = 64;     // query rows per Q tile
 constexpr int BNB = 128;    // keys per KV tile
@@ -195,6 +194,7 @@ __global__ __launch_bounds__(NTK) void attn_bwd_kv_kernel(BwdParams p) {
   const WorkItem kt = p.work[w];
   const WorkRange rg = p.range[w];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // the same, in a scalar register
   const int k4 = wave & 3, qb = wave >> 2;           // key group (32 keys) and Q row block (32 rows)
 
   // this wave's keys: local key index k4*32 + l32 within the tile
@@ -222,9 +222,9 @@ __global__ __launch_bounds__(NTK) void attn_bwd_kv_kernel(BwdParams p) {
       const int P = (i * NW + wave) * 64 + lane;
       const int row = P / RT::CPR;
       const int64_t off = kv_base + int64_t(min(row, kt.n - 1)) * p.kv_row_stride + 8 * ((P % RT::CPR) ^ RT::sw(row));
-      const int dst = (i * NW + wave) * 1024;
-      __builtin_amdgcn_global_load_lds((global_void *)(p.k + off), (lds_void *)(lds + dst), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((global_void *)(p.v + off), (lds_void *)(lds + KVT + dst), 16, 0, 0);
+      const int dst = (i * NW + wave_s) * 1024;
+      copy_to_lds(p.k + off, lds, dst);
+      copy_to_lds(p.v + off, lds, KVT + dst);
     }
   }
   constexpr int LOADS = BMB * RT::CPR / NTK;
@@ -279,17 +279,15 @@ __global__ __launch_bounds__(NTK) void attn_bwd_kv_kernel(BwdParams p) {
     const const_entry &e = cpart[__builtin_amdgcn_readfirstlane(pbase + itr / p.group)];
     return PartnerEntry{e.local_start, e.global_start, e.n, e.cls};
   };
-  auto issue_rows = [&](int itr, unsigned char *stage) {
+  auto issue_rows = [&](int itr, int stage) {   // stage: byte offset in lds
     const PartnerEntry t = entry(itr);
     const int hh = g * p.group + itr % p.group;
     const int64_t base = int64_t(t.local_start) * p.q_row_stride + int64_t(hh) * D;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int64_t off = base + int64_t(min(src_row[i], t.n - 1)) * p.q_row_stride + src_col[i];
-      lds_void *dq = (lds_void *)(stage + KS::Q + (i * NW + wave) * 1024);
-      lds_void *dd = (lds_void *)(stage + KS::DO + (i * NW + wave) * 1024);
-      __builtin_amdgcn_global_load_lds((global_void *)(p.q + off), dq, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((global_void *)(p.dout + off), dd, 16, 0, 0);
+      copy_to_lds(p.q + off, lds, stage + KS::Q + (i * NW + wave_s) * 1024);
+      copy_to_lds(p.dout + off, lds, stage + KS::DO + (i * NW + wave_s) * 1024);
     }
   };
   // per-row terms of one iteration (threads 0..BMB-1, one row each): loaded
@@ -316,11 +314,12 @@ __global__ __launch_bounds__(NTK) void attn_bwd_kv_kernel(BwdParams p) {
     reinterpret_cast<int *>(stage + KS::DS)[tid] = rt_s;
   };
 
-  issue_rows(0, lds + ST0);
+  issue_rows(0, ST0);
   if (tid < BMB) {
     load_terms(0);
     store_terms(lds + ST0);
   }
+  wait_copies();
   __syncthreads();
 
   for (int itr = 0; itr < n_iter; ++itr) {
@@ -353,7 +352,7 @@ __global__ __launch_bounds__(NTK) void attn_bwd_kv_kernel(BwdParams p) {
     // work through S and dP (all waves issue them at the same point, and the
     // memory pipeline takes them in turn)
     if (more) {
-      issue_rows(itr + 1, nxt);
+      issue_rows(itr + 1, ST0 + ((itr + 1) & 1) * STAGE);
       if (tid < BMB) load_terms(itr + 1);
     }
 
@@ -419,49 +418,32 @@ __global__ __launch_bounds__(NTK) void attn_bwd_kv_kernel(BwdParams p) {
 
     // ---- dV^T += dO^T P, dK^T += Q^T dS (k = 16 query rows per step; the
     //      rows of step u are qb*32 + 16u + 4hf + (0..3 | 8..11))
-    //      The transposing reads go through inline asm with explicit waits:
-    //      the compiler cannot tell them apart from the in-flight copies into
-    //      the other stage and would wait for those first.
     {
-      // one address per 32-column block and read of a pair; the tile (dO or
-      // Q) and the 16-row step go into the instructions' immediate offsets
-      const unsigned cbase = static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_void *)cur));
-      unsigned a_lo[D / 32], a_hi[D / 32];
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        a_lo[db] = cbase + t_lo[db];
-        a_hi[db] = cbase + t_hi[db];
-      }
-      auto issue = [](auto kc, const unsigned (&lo)[D / 32], const unsigned (&hi)[D / 32], u32x2 (&r)[4]) {
-        constexpr int k = decltype(kc)::value;
-        constexpr int u = k / (D / 32), db = k % (D / 32);
-        constexpr int odo = KS::DO + 16 * u * RT::ROW, oq = KS::Q + 16 * u * RT::ROW;
-        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r[0]) : "v"(lo[db]), "n"(odo));
-        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r[1]) : "v"(hi[db]), "n"(odo));
-        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r[2]) : "v"(lo[db]), "n"(oq));
-        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r[3]) : "v"(hi[db]), "n"(oq));
+      // one offset per 32-column block and read of a pair; the tile (dO or
+      // Q) and the 16-row step are constants the reads take as immediates
+      auto rd = [&](int t, int imm) { return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(cur + t + imm)); };
+      auto join = [](const i16x4 &lo, const i16x4 &hi) {
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       };
-      auto join = [](const u32x2 &lo, const u32x2 &hi) { return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y}); };
-      u32x2 rr[2][4];
-      issue(std::integral_constant<int, 0>{}, a_lo, a_hi, rr[0]);
       static_for<2 * (D / 32)>([&](auto kc) {
         constexpr int k = decltype(kc)::value;
         constexpr int u = k / (D / 32), db = k % (D / 32);
-        u32x2 (&r)[4] = rr[k & 1];
-        if constexpr (k + 1 < 2 * (D / 32)) {
-          issue(std::integral_constant<int, k + 1>{}, a_lo, a_hi, rr[(k + 1) & 1]);
-          asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
-        } else {
-          asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
-        }
-        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(r[0], r[1]), pb[u], dva[db], 0, 0, 0);
-        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(r[2], r[3]), sb[u], dka[db], 0, 0, 0);
+        constexpr int odo = KS::DO + 16 * u * RT::ROW, oq = KS::Q + 16 * u * RT::ROW;
+        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(rd(t_lo[db], odo), rd(t_hi[db], odo)), pb[u], dva[db], 0, 0, 0);
+        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(rd(t_lo[db], oq), rd(t_hi[db], oq)), sb[u], dka[db], 0, 0, 0);
+      });
+      // schedule: the reads of step k + 1 go out before the products of step k
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      static_for<2 * (D / 32)>([&](auto kc) {
+        __builtin_amdgcn_sched_group_barrier(0x100, decltype(kc)::value + 1 < 2 * (D / 32) ? 4 : 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       });
     }
 
     // the next iteration's row terms (loaded above, latency hidden by the math)
     if (more && tid < BMB) store_terms(nxt);
     // copies for the next iteration have landed and every wave is done with this stage
+    wait_copies();
     __syncthreads();
   }
 
@@ -619,6 +601,7 @@ __global__ __launch_bounds__(2 * TQ * NH) void attn_bwd_dq_kernel(BwdParams p) {
   const int w = G / p.hkv, g = G % p.hkv;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // the same, in a scalar register
   const int h = g * p.group + (slot % pairs) * NH + wave / WPH;
   const WorkItem qt = p.work[w];
   const WorkRange rg = p.range[w];
@@ -670,15 +653,15 @@ __global__ __launch_bounds__(2 * TQ * NH) void attn_bwd_dq_kernel(BwdParams p) {
       t_off[db] = row * RT::ROW + 16 * ((col >> 3) ^ RT::sw(row)) + 2 * (col & 7);
     }
   }
-  auto issue_half = [&](const PartnerEntry &kt, int half, unsigned char *stage) {
+  auto issue_half = [&](const PartnerEntry &kt, int half, int stage) {   // stage: byte offset in lds
     const int kn = min(HKQ, kt.n - half * HKQ);
     const int64_t base = int64_t(kt.local_start + half * HKQ) * p.kv_row_stride + int64_t(g) * D;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int64_t off = base + int64_t(min(src_row[i], kn - 1)) * p.kv_row_stride + src_col[i];
-      const int dst = (i * NWV + wave) * 1024;
-      __builtin_amdgcn_global_load_lds((global_void *)(p.k + off), (lds_void *)(stage + KOFF + dst), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((global_void *)(p.v + off), (lds_void *)(stage + VOFF + dst), 16, 0, 0);
+      const int dst = (i * NWV + wave_s) * 1024;
+      copy_to_lds(p.k + off, lds, stage + KOFF + dst);
+      copy_to_lds(p.v + off, lds, stage + VOFF + dst);
     }
   };
 
@@ -694,7 +677,8 @@ __global__ __launch_bounds__(2 * TQ * NH) void attn_bwd_dq_kernel(BwdParams p) {
 
   // iterations: the 64-key halves of the partner tiles, in order
   int it = 0, half = 0, stage_i = 0;
-  if (rg.count > 0) issue_half(entry(0), 0, lds);
+  if (rg.count > 0) issue_half(entry(0), 0, 0);
+  wait_copies();
   __syncthreads();
   while (it < rg.count) {
     const PartnerEntry kt = entry(it);
@@ -718,41 +702,15 @@ __global__ __launch_bounds__(2 * TQ * NH) void attn_bwd_dq_kernel(BwdParams p) {
       if (kt.cls == SAP_TILE_PARTIAL) lo = dsq - (kt.global_start + k0);
     }
     const int hi_r = hi - 4 * hf, lo_r = lo - 4 * hf;
-    constexpr int NR = 2 * (D / 32);
-    // transposing reads of K^T: one address per 32-column block and read of
-    // a pair, the 16-key step in the instructions' immediate offsets; inline
-    // asm with explicit waits (the compiler cannot tell them apart from the
-    // in-flight copies into the other stage and would wait for those first)
-    const unsigned kbase = static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_void *)(cur + KOFF)));
-    unsigned a_lo[D / 32], a_hi[D / 32];
+    // transposing reads of K^T: one offset per 32-column block and read of
+    // a pair, the 16-key step a constant the reads take as an immediate
+    int k_lo[D / 32], k_hi[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      a_lo[db] = kbase + t_off[db];
-      a_hi[db] = kbase + (RT::CPR >= 16 ? (t_off[db] ^ RT::TR8) : t_off[db]) + 8 * RT::ROW;
+      k_lo[db] = KOFF + t_off[db];
+      k_hi[db] = KOFF + (RT::CPR >= 16 ? (t_off[db] ^ RT::TR8) : t_off[db]) + 8 * RT::ROW;
     }
-    auto issue = [](auto sc, const unsigned (&lo_)[D / 32], const unsigned (&hi_)[D / 32], u32x2 (&r)[NR]) {
-      constexpr int off = 16 * decltype(sc)::value * RT::ROW;   // kb * 32 + 16 u rows
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r[2 * db]) : "v"(lo_[db]), "n"(off));
-        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r[2 * db + 1]) : "v"(hi_[db]), "n"(off));
-      }
-    };
-    auto wait_reads = [](auto keep, u32x2 (&r)[NR]) {
-      if constexpr (decltype(keep)::value) {
-        if constexpr (NR == 8)
-          asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]),
-                       "+v"(r[5]), "+v"(r[6]), "+v"(r[7]));
-        else
-          asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
-      } else {
-        if constexpr (NR == 8)
-          asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]),
-                       "+v"(r[5]), "+v"(r[6]), "+v"(r[7]));
-        else
-          asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
-      }
-    };
+    auto rd = [&](int t, int imm) { return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(cur + t + imm)); };
     static_for<KBQ>([&](auto kbc) {
       constexpr int kb = decltype(kbc)::value;
       // ---- S^T = K Q^T, dP^T = V dO^T (32 keys x this wave's 32 queries)
@@ -769,7 +727,7 @@ __global__ __launch_bounds__(2 * TQ * NH) void attn_bwd_dq_kernel(BwdParams p) {
       // the first block's S^T and dP^T (all waves issue them at the same
       // point, and the memory pipeline takes them in turn)
       if constexpr (kb == 0)
-        if (nit < rg.count) issue_half(entry(nit), nhalf, lds + (stage_i ^ 1) * STAGE);
+        if (nit < rg.count) issue_half(entry(nit), nhalf, (stage_i ^ 1) * STAGE);
       // ---- dS^T = P^T o (dP^T - D); element i is key k0 + kb*32 + 8*(i/4) + 4*hf + (i%4)
       bf16x8 sb[2];
       auto ds_t = [&](auto mask_tag) {
@@ -802,21 +760,19 @@ __global__ __launch_bounds__(2 * TQ * NH) void attn_bwd_dq_kernel(BwdParams p) {
       else
         ds_t(std::false_type{});
       // ---- dQ^T += K^T dS^T (k = 16 keys per step: kb*32 + 16u + 4hf + (0..3 | 8..11))
-      u32x2 rr[2][NR];
-      issue(std::integral_constant<int, 2 * kb>{}, a_lo, a_hi, rr[0]);
-      issue(std::integral_constant<int, 2 * kb + 1>{}, a_lo, a_hi, rr[1]);
       static_for<2>([&](auto uc) {
-        constexpr int u = decltype(uc)::value;
-        wait_reads(std::integral_constant<bool, u == 0>{}, rr[u]);
+        constexpr int off = 16 * (2 * kb + decltype(uc)::value) * RT::ROW;   // kb * 32 + 16 u rows
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 ak = as_bf16x8(u32x4{rr[u][2 * db].x, rr[u][2 * db].y, rr[u][2 * db + 1].x, rr[u][2 * db + 1].y});
-          qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, sb[u], qacc[db], 0, 0, 0);
+          const i16x4 lo = rd(k_lo[db], off), hi = rd(k_hi[db], off);
+          const bf16x8 ak = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, sb[decltype(uc)::value], qacc[db], 0, 0, 0);
         }
       });
     });
 
     // the next half's copies have landed and every wave is done with this stage
+    wait_copies();
     __syncthreads();
     stage_i ^= 1;
     it = nit;

@@ -56,6 +56,7 @@
 #include <type_traits>
 
 #include "kernels.h"
+#include "lds_copy.h"
 
 namespace sap {
 namespace {
@@ -66,8 +67,6 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void global_void;
 
 constexpr int BN = 64;
 constexpr int NXCD = 8;
@@ -138,27 +137,26 @@ __device__ inline LoadOffsets<D, NT> load_offsets(int stride, int wave, int lane
 }
 
 // Issues the direct global -> LDS copies of one KV tile's K rows (V = false)
-// or V rows (V = true) into a stage.
+// or V rows (V = true) into the stage at byte offset stage of lds.
 template <int D, int NT, bool V>
-__device__ inline void issue_half(const FwdParams &p, const PartnerEntry &pe, int g, unsigned char *stage,
-                                  int wave, int lane, const LoadOffsets<D, NT> &full) {
+__device__ inline void issue_half(const FwdParams &p, const PartnerEntry &pe, int g, const unsigned char *lds,
+                                  int stage, int wave, int lane, const LoadOffsets<D, NT> &full) {
   using G = Stage<D, NT>;
   const int64_t base = int64_t(pe.local_start) * p.kv_row_stride + int64_t(g) * D;
   const unsigned short *src = (V ? p.v : p.k) + base;
   const LoadOffsets<D, NT> o = pe.n == BN ? full : load_offsets<D, NT>(int(p.kv_row_stride), wave, lane, pe.n);
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
   for (int i = 0; i < G::LOADS; ++i)
-    __builtin_amdgcn_global_load_lds((global_void *)(src + (V ? o.v[i] : o.k[i])),
-                                     (lds_void *)(stage + (V ? G::TILE : 0) + (i * (NT / 64) + wave) * 1024),
-                                     16, 0, 0);
+    copy_to_lds(src + (V ? o.v[i] : o.k[i]), lds, stage + (V ? G::TILE : 0) + (i * (NT / 64) + wave_s) * 1024);
 }
 
 // The same copies issued by four waves of an eight-wave workgroup (c = 0..3
 // numbers them): chunk position P = (i * 4 + c) * 64 + lane, offsets
 // computed here (nothing held in registers across the loop).
 template <int D, int NT, bool V>
-__device__ inline void issue_half_by4(const FwdParams &p, const PartnerEntry &pe, int g, unsigned char *stage, int c,
-                                      int lane) {
+__device__ inline void issue_half_by4(const FwdParams &p, const PartnerEntry &pe, int g, const unsigned char *lds,
+                                      int stage, int c, int lane) {
   using G = Stage<D, NT>;
   constexpr int L4 = BN * G::CPR / 256;
   const int64_t base = int64_t(pe.local_start) * p.kv_row_stride + int64_t(g) * D;
@@ -169,8 +167,7 @@ __device__ inline void issue_half_by4(const FwdParams &p, const PartnerEntry &pe
     const int P = (i * 4 + c) * 64 + lane;
     const int row = P / G::CPR, pos = P % G::CPR;
     const int off = min(row, pe.n - 1) * stride + 8 * (pos ^ (V ? G::vsw(row) : G::ksw(row)));
-    __builtin_amdgcn_global_load_lds((global_void *)(src + off), (lds_void *)(stage + (V ? G::TILE : 0) + (i * 4 + c) * 1024),
-                                     16, 0, 0);
+    copy_to_lds(src + off, lds, stage + (V ? G::TILE : 0) + (i * 4 + c) * 1024);
   }
 }
 
@@ -391,9 +388,10 @@ __global__ __launch_bounds__(2 * TM * NH) __attribute__((amdgpu_waves_per_eu(2))
     const bool copier = ((wave_u >> 2) ^ wave_u) & 1;
     const int copier_id = wave_u >> 1;
     PartnerEntry e2 = uniform(raw(2));
-    issue_half<D, NT, false>(p, e0, g, lds, wave, lane, full_offs);
-    issue_half<D, NT, true>(p, e0, g, lds, wave, lane, full_offs);
-    if (cnt > 1) issue_half<D, NT, false>(p, e1, g, lds + ST::BYTES, wave, lane, full_offs);
+    issue_half<D, NT, false>(p, e0, g, lds, 0, wave, lane, full_offs);
+    issue_half<D, NT, true>(p, e0, g, lds, 0, wave, lane, full_offs);
+    if (cnt > 1) issue_half<D, NT, false>(p, e1, g, lds, ST::BYTES, wave, lane, full_offs);
+    wait_copies();
     __syncthreads();
     f32x16 sA[2], sB[2];
     scores(sA, lds);
@@ -401,19 +399,20 @@ __global__ __launch_bounds__(2 * TM * NH) __attribute__((amdgpu_waves_per_eu(2))
 
     auto body = [&](f32x16 (&s)[2], f32x16 (&s_next)[2], int j, auto has_next) {
       constexpr bool HN = decltype(has_next)::value;
-      unsigned char *stage_j = lds + (j & 1) * ST::BYTES;
-      unsigned char *stage_n = lds + ((j + 1) & 1) * ST::BYTES;
+      const int off_j = (j & 1) * ST::BYTES, off_n = ((j + 1) & 1) * ST::BYTES;
+      const unsigned char *stage_j = lds + off_j, *stage_n = lds + off_n;
       // one wave of each pair that shares a SIMD issues the copies (twice as
       // many); its partner starts on the tile meanwhile
       if (copier) {
-        if (j + 2 < cnt) issue_half_by4<D, NT, false>(p, e2, g, stage_j, copier_id, lane);
-        if (HN) issue_half_by4<D, NT, true>(p, e1, g, stage_n, copier_id, lane);
+        if (j + 2 < cnt) issue_half_by4<D, NT, false>(p, e2, g, lds, off_j, copier_id, lane);
+        if (HN) issue_half_by4<D, NT, true>(p, e1, g, lds, off_n, copier_id, lane);
       }
       const PartnerEntry raw3 = raw(j + 3);
       tile_math(s, e0, stage_j, [&] {
         if (HN) scores(s_next, stage_n);
       });
       // the copies have landed and every wave is done with this iteration's slots
+      wait_copies();
       __syncthreads();
       // nothing moves above the barrier: the entry load's wait stays behind it
       __builtin_amdgcn_sched_barrier(0);
@@ -439,20 +438,22 @@ __global__ __launch_bounds__(2 * TM * NH) __attribute__((amdgpu_waves_per_eu(2))
     // Four waves (more workgroups per CU, which overlap one another's
     // phases): plain double buffer; the next tile's K and V are copied
     // while this tile is computed.
-    issue_half<D, NT, false>(p, e0, g, lds, wave, lane, full_offs);
-    issue_half<D, NT, true>(p, e0, g, lds, wave, lane, full_offs);
+    issue_half<D, NT, false>(p, e0, g, lds, 0, wave, lane, full_offs);
+    issue_half<D, NT, true>(p, e0, g, lds, 0, wave, lane, full_offs);
+    wait_copies();
     __syncthreads();
     for (int j = 0; j < cnt; ++j) {
-      unsigned char *stage_j = lds + (j & 1) * ST::BYTES;
-      unsigned char *stage_n = lds + ((j + 1) & 1) * ST::BYTES;
+      const unsigned char *stage_j = lds + (j & 1) * ST::BYTES;
+      const int off_n = ((j + 1) & 1) * ST::BYTES;
       if (j + 1 < cnt) {
-        issue_half<D, NT, false>(p, e1, g, stage_n, wave, lane, full_offs);
-        issue_half<D, NT, true>(p, e1, g, stage_n, wave, lane, full_offs);
+        issue_half<D, NT, false>(p, e1, g, lds, off_n, wave, lane, full_offs);
+        issue_half<D, NT, true>(p, e1, g, lds, off_n, wave, lane, full_offs);
       }
       const PartnerEntry raw2 = raw(j + 2);
       f32x16 s[2];
       scores(s, stage_j);
       tile_math(s, e0, stage_j, [] {});
+      wait_copies();
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
       e0 = e1;
