@@ -24,9 +24,9 @@
 //     A operand is two ds_read_b64_tr_b16 transposing reads of 4 keys each
 //     from row-major V.
 //   * K and V tiles go from global memory straight into LDS
-//     (global_load_lds_dwordx4: no registers, no VALU) into a double buffer;
-//     copies issued in an iteration are waited for at the barrier that ends
-//     it. Each load instruction fills 1 KB of LDS, 16 bytes per lane in lane
+//     (global_load_lds_dwordx4 through copy_to_lds: no registers, no VALU)
+//     into a double buffer; copies issued in an iteration are waited for at
+//     the barrier that ends it. Each load instruction fills 1 KB of LDS, 16 bytes per lane in lane
 //     order, so the layout is chosen through the global address each lane
 //     loads: rows are unpadded and the 16-byte chunks of a row are
 //     XOR-swizzled by the row index, which keeps the matrix-operand reads
@@ -382,8 +382,8 @@ __global__ __launch_bounds__(2 * TM * NH) __attribute__((amdgpu_waves_per_eu(2))
     // slot), turns S_j into P_j on the vector ALUs while the matrix cores
     // compute S_{j+1}, adds V_j P_j into O, and ends at a barrier that makes
     // its copies visible and frees the slots it read.
-    // waves 1, 3, 4, 6: one of each pair (w, w + 4) and of each pair
-    // (2i, 2i + 1), whichever pairs share a SIMD
+    // waves 1, 3, 4, 6: one of each pair (w, w + 4), the two waves a SIMD
+    // holds (the choice also takes one of each pair (2i, 2i + 1))
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const bool copier = ((wave_u >> 2) ^ wave_u) & 1;
     const int copier_id = wave_u >> 1;
