@@ -10,6 +10,11 @@
 // allocates can be overwritten by a copy in flight. The kernels copy into a
 // stage only when no wave reads it, and wait for their copies themselves
 // (wait_copies) before the barrier that hands the stage to the other waves.
+// The statement declares no memory effect: its order against the LDS reads
+// comes from those barriers (a stage is copied into only after the barrier
+// that ends every read of it, and read only after the barrier that follows
+// the wait), so keep every copy and every read of one stage on opposite
+// sides of a barrier.
 #pragma once
 
 #include <hip/hip_runtime.h>
